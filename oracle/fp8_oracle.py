@@ -1,0 +1,286 @@
+"""CPU oracle for the grouped FP8 (e4m3) block-scaled GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, tables or
+constants with the HIP library; it is plain numpy in float64.
+
+What it computes follows the first page of the reference material, the FlyDSL
+pull request "Grouped and Batched GEMM kernels with blockscaling matching
+DeepGEMM API" (sections "Summary" and "DeepGEMM conformance details"):
+
+* activations carry one scale per token per 128 channels (a (1,128) block),
+  stored transposed as ``[ceil(K/128), M]``;
+* weights carry one scale per (128,128) block;
+* scales are E8M0 (a bare power of two) rounded *up* (``ceil_to_ue8m0``) so
+  that ``|x / scale|`` never exceeds the FP8 maximum 448;
+* the contiguous op maps each row of A to an expert through
+  ``grouped_layout`` (-1 marks padding rows); the masked op computes, for each
+  group g, only rows ``m < masked_m[g]`` of a ``[G, M_max, K]`` batch;
+* ``D[g] = A[g] . B[g]^T`` ("nt": K is the contiguous axis of both operands).
+
+The scales are powers of two and are applied exactly, so the method reaches
+"dequantize, then multiply" up to summation order; that plain definition is
+what this module writes out (dequantize exactly in float64, multiply with a
+float64 matmul).
+
+Readings of points the pages leave open (each one is also listed in the
+design notes of the repository):
+
+* FP8 is OCP E4M3FN (bias 7, max 448, no infinity, NaN = S.1111.111); the
+  page fixes the maximum as 448 but not the rounding.  Rounding is
+  round-to-nearest, ties to the even code.
+* ``ceil_to_ue8m0`` is taken exactly: the scale exponent t is the smallest
+  integer with ``448 * 2**t >= amax``.  An all-zero block gets t = 0
+  (byte 127); a block whose t falls outside the E8M0 range [-127, 127] is
+  an error.
+* ``calc_diff`` ("cosine-similarity-style normalized error") is
+  ``1 - 2*sum(x*y) / sum(x*x + y*y)``.
+* Rows that are padding (``grouped_layout`` outside [0, G)) or masked off
+  (``m >= masked_m[g]``) keep whatever the output buffer held.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+FP8_MAX = 448.0          # largest finite E4M3FN value (page 1, conformance section)
+BLOCK = 128              # scale block edge along K (and along N for weights)
+
+
+# ---------------------------------------------------------------- FP8 E4M3FN
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Value of each E4M3FN byte, in float64 (OCP FP8 definition).
+
+    sign = bit 7, exponent = bits 6..3 (bias 7), mantissa = bits 2..0.
+    exponent 0 is subnormal: m * 2**-9.  exponent 15 with mantissa 7 is NaN.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7 == 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    normal = (1.0 + m / 8.0) * np.exp2(e - 7.0)
+    sub = m * 2.0 ** -9
+    val = sign * np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def encode_e4m3_rne(x: np.ndarray) -> np.ndarray:
+    """Nearest E4M3FN code to each float64 value, ties to the even code.
+
+    Inputs must satisfy |x| <= 448 (the quantizer guarantees it).  The
+    spacing of representable values is 2**(E-3) in the binade [2**E, 2**(E+1))
+    for E >= -6 and 2**-9 below 2**-6 (subnormals); dividing by that power of
+    two is exact, and ``np.rint`` rounds half to even, which is the even
+    mantissa code.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("encode_e4m3_rne: non-finite input")
+    if np.any(np.abs(x) > FP8_MAX):
+        raise ValueError("encode_e4m3_rne: |x| > 448")
+    a = np.abs(x)
+    _, p = np.frexp(a)                          # a = f * 2**p, f in [0.5, 1)
+    E = np.maximum(p - 1, -6)                   # binade exponent, subnormals share -6
+    quantum = np.exp2(E - 3.0)
+    r = np.rint(a / quantum) * quantum          # rounded magnitude, exact
+    _, p2 = np.frexp(r)
+    E2 = np.where(r >= 2.0 ** -6, p2 - 1, 0)
+    mant = np.where(r >= 2.0 ** -6, r / np.exp2(E2.astype(np.float64)) * 8 - 8, r * 2.0 ** 9)
+    expo = np.where(r >= 2.0 ** -6, E2 + 7, 0)
+    code = (expo.astype(np.int64) << 3) | mant.astype(np.int64)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    if np.any((code & 0x7F) > 0x7E):
+        raise ValueError("encode_e4m3_rne: rounded past 448")
+    return code.astype(np.uint8)
+
+
+# ---------------------------------------------------------------- E8M0 scale
+def e8m0_ceil_exponent(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer t with 448 * 2**t >= amax (t = 0 where amax == 0).
+
+    This is ``ceil(log2(amax / 448))`` evaluated exactly: start one below the
+    frexp estimate and step up while the bound fails.  Every comparison is
+    exact in float64 because 448 * 2**t is a power-of-two multiple of 448.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    if np.any(~np.isfinite(amax)) or np.any(amax < 0):
+        raise ValueError("e8m0_ceil_exponent: amax must be finite and >= 0")
+    _, p = np.frexp(np.where(amax > 0, amax, 1.0))
+    t = p.astype(np.int64) - 10                 # 448 = 0.875 * 2**9, so t >= p - 10
+    for _ in range(4):
+        t = np.where(FP8_MAX * np.exp2(t.astype(np.float64)) < amax, t + 1, t)
+    assert np.all(FP8_MAX * np.exp2(t.astype(np.float64)) >= amax)
+    t = np.where(amax > 0, t, 0)
+    if np.any(t < -127) or np.any(t > 127):
+        raise ValueError("e8m0_ceil_exponent: scale outside the E8M0 range")
+    return t
+
+
+def e8m0_value(byte: np.ndarray) -> np.ndarray:
+    """2**(b - 127) for an E8M0 byte b; 255 is NaN."""
+    b = np.asarray(byte, dtype=np.int64)
+    return np.where(b == 255, np.nan, np.exp2(b - 127.0))
+
+
+# ---------------------------------------------------------------- quantizers
+def _pad_to(x: np.ndarray, axis: int, mult: int) -> np.ndarray:
+    n = x.shape[axis]
+    extra = (-n) % mult
+    if extra == 0:
+        return x
+    widths = [(0, 0)] * x.ndim
+    widths[axis] = (0, extra)
+    return np.pad(x, widths)
+
+
+def quantize_act_1x128(x: np.ndarray):
+    """Per-token (1,128) quantization of activations x[M, K] (float32).
+
+    Returns ``(q [M, K] uint8 e4m3, scale_t [ceil(K/128), M] uint8 e8m0)``:
+    for every row m and K-block kb, amax = max |x[m, 128kb : 128kb+128]|,
+    t = e8m0 exponent of amax, byte = t + 127, q = RNE_e4m3(x / 2**t).
+    The scale is stored transposed, [K-block, row], as the page specifies.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    M, K = x.shape
+    kb = -(-K // BLOCK)
+    xp = _pad_to(x, 1, BLOCK).reshape(M, kb, BLOCK)
+    amax = np.abs(xp).max(axis=2)                       # [M, kb]
+    t = e8m0_ceil_exponent(amax)                        # [M, kb]
+    q = encode_e4m3_rne(xp / np.exp2(t[:, :, None].astype(np.float64)))
+    q = q.reshape(M, kb * BLOCK)[:, :K]
+    return np.ascontiguousarray(q), np.ascontiguousarray((t + 127).astype(np.uint8).T)
+
+
+def quantize_weight_128x128(w: np.ndarray):
+    """Per-block (128,128) quantization of weights w[G, N, K] (float32).
+
+    Returns ``(q [G, N, K] uint8 e4m3, scale [G, ceil(N/128), ceil(K/128)] uint8)``.
+    One scale per (group, N-block, K-block), K-block fastest in memory.
+    """
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    G, N, K = w.shape
+    nb, kb = -(-N // BLOCK), -(-K // BLOCK)
+    wp = _pad_to(_pad_to(w, 1, BLOCK), 2, BLOCK).reshape(G, nb, BLOCK, kb, BLOCK)
+    amax = np.abs(wp).max(axis=(2, 4))                  # [G, nb, kb]
+    t = e8m0_ceil_exponent(amax)
+    q = encode_e4m3_rne(wp / np.exp2(t[:, :, None, :, None].astype(np.float64)))
+    q = q.reshape(G, nb * BLOCK, kb * BLOCK)[:, :N, :K]
+    return np.ascontiguousarray(q), (t + 127).astype(np.uint8)
+
+
+def dequantize_act(q: np.ndarray, scale_t: np.ndarray) -> np.ndarray:
+    """A_dq[m, k] = e4m3(q[m, k]) * 2**(scale_t[k // 128, m] - 127), float64."""
+    M, K = q.shape
+    s = e8m0_value(scale_t).T                            # [M, kb]
+    return decode_e4m3(q) * np.repeat(s, BLOCK, axis=1)[:, :K]
+
+
+def dequantize_weight(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """B_dq[g, n, k] = e4m3(q[g, n, k]) * 2**(scale[g, n // 128, k // 128] - 127)."""
+    G, N, K = q.shape
+    s = e8m0_value(scale)
+    s = np.repeat(np.repeat(s, BLOCK, axis=1), BLOCK, axis=2)[:, :N, :K]
+    return decode_e4m3(q) * s
+
+
+# ---------------------------------------------------------------- grouped GEMMs
+def grouped_gemm_contiguous(q_a, scale_a, q_b, scale_b, grouped_layout, d_init=None):
+    """Contiguous grouped GEMM, float64.
+
+    For each expert g: ``D[rows with grouped_layout == g] = A_dq[rows] @ B_dq[g]^T``.
+    Rows whose layout entry is outside [0, G) (padding, -1) keep ``d_init``
+    (NaN when no initial buffer is given).
+    """
+    a = dequantize_act(q_a, scale_a)
+    b = dequantize_weight(q_b, scale_b)
+    layout = np.asarray(grouped_layout, dtype=np.int64)
+    M, N = a.shape[0], b.shape[1]
+    d = np.full((M, N), np.nan) if d_init is None else np.array(d_init, dtype=np.float64)
+    for g in range(b.shape[0]):
+        rows = np.nonzero(layout == g)[0]
+        if rows.size:
+            d[rows] = a[rows] @ b[g].T
+    return d
+
+
+def grouped_gemm_masked(q_a, scale_a, q_b, scale_b, masked_m, d_init=None):
+    """Masked grouped GEMM, float64.
+
+    q_a is [G, M_max, K] with scale_a [G, ceil(K/128), M_max]; for each group g
+    only rows ``m < masked_m[g]`` (clamped to [0, M_max]) are computed:
+    ``D[g, :mm] = A_dq[g, :mm] @ B_dq[g]^T``; other rows keep ``d_init``.
+    """
+    G, Mmax, K = q_a.shape
+    b = dequantize_weight(q_b, scale_b)
+    N = b.shape[1]
+    d = np.full((G, Mmax, N), np.nan) if d_init is None else np.array(d_init, dtype=np.float64)
+    for g in range(G):
+        mm = int(min(max(int(masked_m[g]), 0), Mmax))
+        if mm:
+            a = dequantize_act(q_a[g, :mm], scale_a[g][:, :mm])
+            d[g, :mm] = a @ b[g].T
+    return d
+
+
+def quantize_act_masked(x: np.ndarray):
+    """Per-group (1,128) quantization of a masked batch x[G, M_max, K].
+
+    Returns ``(q [G, M_max, K], scale_t [G, ceil(K/128), M_max])``: the page's
+    transposed activation-scale layout, one such matrix per group.
+    """
+    qs, ss = zip(*(quantize_act_1x128(xg) for xg in np.asarray(x)))
+    return np.stack(qs), np.stack(ss)
+
+
+# ---------------------------------------------------------------- metrics
+def calc_diff(x, y) -> float:
+    """1 - 2*sum(x*y) / sum(x*x + y*y), in float64 ("cosine-similarity-style")."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    y = np.asarray(y, dtype=np.float64).ravel()
+    denom = np.sum(x * x + y * y)
+    if denom == 0.0:
+        return 0.0
+    return float(1.0 - 2.0 * np.sum(x * y) / denom)
+
+
+def max_rel_err_rowfloor(got, ref, floor: float = 1e-3) -> float:
+    """max |got - ref| / max(|ref|, floor * max_n |ref[m, n]|) over all elements.
+
+    The denominator is floored per row (per token), which matches the
+    per-token scaling: an output near zero is judged against the size of
+    its row rather than against itself.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rowmax = np.abs(ref).max(axis=-1, keepdims=True)
+    den = np.maximum(np.abs(ref), floor * rowmax)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(got - ref) / den))
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (ties to even), as float64.
+
+    bfloat16 keeps 8 significant bits; the spacing in binade [2**E, 2**(E+1))
+    is 2**(E-7).  Exact for inputs inside the bfloat16 normal range.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, p = np.frexp(np.where(a > 0, a, 1.0))
+    quantum = np.exp2(np.maximum(p - 1, -126) - 7.0)
+    return np.copysign(np.rint(a / quantum) * quantum, x)
+
+
+def round_to_f16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest IEEE half (ties to even), as float64.
+
+    Half keeps 11 significant bits; spacing 2**(E-10), subnormal spacing 2**-24.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, p = np.frexp(np.where(a > 0, a, 1.0))
+    quantum = np.exp2(np.maximum(p - 1, -14) - 10.0)
+    return np.copysign(np.rint(a / quantum) * quantum, x)

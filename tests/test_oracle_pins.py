@@ -1,0 +1,403 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test ties a part of the oracle to something fixed outside it: the OCP
+FP8 format definition (hand-derived golden files), a library cast (torch's
+float8_e4m3fn / bfloat16, numpy's float16), brute force on tiny inputs in
+pure Python, closed forms, exact integer arithmetic and the error bound the
+first reference page states (calc_diff <= 1e-3 against the pre-quantization
+FP32 product, section "DeepGEMM conformance details").
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8_oracle as o
+from fp8_block_scaled_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split()[:2])
+    return rows
+
+
+# ------------------------------------------------------------------ brute force helpers
+def _all_e4m3_values():
+    """(code, value) for every finite E4M3FN code, from the bit-field definition."""
+    out = []
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        out.append((c, -v if s else v))
+    return out
+
+
+_TABLE = _all_e4m3_values()
+
+
+def _bf_encode(x: float) -> int:
+    """Nearest finite E4M3FN code by exhaustive search; ties go to the even code."""
+    best = None
+    for c, v in _TABLE:
+        if v == 0.0 and (c >> 7) != (1 if math.copysign(1, x) < 0 else 0):
+            continue  # keep the sign of zero
+        d = abs(v - x)
+        key = (d, c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def _bf_exponent(amax: float) -> int:
+    if amax == 0.0:
+        return 0
+    for t in range(-140, 140):
+        if 448.0 * 2.0 ** t >= amax:
+            return t
+    raise AssertionError
+
+
+def _bf_quant_act(x):
+    M, K = x.shape
+    kb = -(-K // 128)
+    q = np.zeros((M, K), np.uint8)
+    s = np.zeros((kb, M), np.uint8)
+    for m in range(M):
+        for b in range(kb):
+            blk = [float(v) for v in x[m, 128 * b:128 * b + 128]]
+            t = _bf_exponent(max(abs(v) for v in blk))
+            s[b, m] = t + 127
+            for j, v in enumerate(blk):
+                q[m, 128 * b + j] = _bf_encode(v / 2.0 ** t)
+    return q, s
+
+
+def _bf_quant_weight(w):
+    G, N, K = w.shape
+    nb, kb = -(-N // 128), -(-K // 128)
+    q = np.zeros((G, N, K), np.uint8)
+    s = np.zeros((G, nb, kb), np.uint8)
+    for g in range(G):
+        for i in range(nb):
+            for b in range(kb):
+                blk = w[g, 128 * i:128 * i + 128, 128 * b:128 * b + 128].astype(np.float64)
+                t = _bf_exponent(float(np.abs(blk).max()))
+                s[g, i, b] = t + 127
+                for r in range(blk.shape[0]):
+                    for j in range(blk.shape[1]):
+                        q[g, 128 * i + r, 128 * b + j] = _bf_encode(float(blk[r, j]) / 2.0 ** t)
+    return q, s
+
+
+def _val(code):
+    return dict(_TABLE)[int(code)]
+
+
+def _bf_gemm_rows(qa, sa, qb, sb, rows_a, g):
+    """fsum triple loop: D[r, n] = sum_k (A value * 2^(sa-127)) * (B value * 2^(sb-127))."""
+    N, K = qb.shape[1], qb.shape[2]
+    out = np.zeros((len(rows_a), N))
+    for i, r in enumerate(rows_a):
+        a = [_val(qa[r, k]) * 2.0 ** (int(sa[k // 128, r]) - 127) for k in range(K)]
+        for n in range(N):
+            out[i, n] = math.fsum(
+                a[k] * _val(qb[g, n, k]) * 2.0 ** (int(sb[g, n // 128, k // 128]) - 127)
+                for k in range(K))
+    return out
+
+
+# ------------------------------------------------------------------ format pins
+def test_decode_golden_codes():
+    for code, val in _read_golden("e4m3_codes.txt"):
+        got = o.decode_e4m3(np.array([int(code, 16)], np.uint8))[0]
+        if val == "nan":
+            assert np.isnan(got)
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), code
+
+
+def test_decode_matches_bitfield_table():
+    codes = np.array([c for c, _ in _TABLE], np.uint8)
+    assert np.array_equal(o.decode_e4m3(codes), np.array([v for _, v in _TABLE]))
+
+
+def test_encode_matches_torch_cast_at_every_midpoint():
+    vals = np.array(sorted({v for _, v in _TABLE}))
+    mids = (vals[1:] + vals[:-1]) / 2          # every tie, exactly representable in f32
+    x = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf)])
+    x = x[np.abs(x) <= 448].astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.encode_e4m3_rne(x.astype(np.float64)), ref)
+
+
+def test_encode_matches_torch_cast_random():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.uniform(-448, 448, 200000),
+                        rng.standard_normal(200000) * 10.0 ** rng.uniform(-4, 2, 200000)])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.encode_e4m3_rne(x.astype(np.float64)), ref)
+
+
+def test_encode_bruteforce_sample():
+    rng = np.random.default_rng(6)
+    x = np.concatenate([rng.uniform(-448, 448, 300), rng.uniform(-0.02, 0.02, 300),
+                        [0.0, -0.0, 448.0, -448.0, 2.0 ** -10, 3 * 2.0 ** -11, 447.99, 2.0 ** -6 - 2.0 ** -11]])
+    got = o.encode_e4m3_rne(x)
+    assert [int(c) for c in got] == [_bf_encode(float(v)) for v in x]
+
+
+def test_encode_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        o.encode_e4m3_rne(np.array([448.5]))
+    with pytest.raises(ValueError):
+        o.encode_e4m3_rne(np.array([np.nan]))
+
+
+def test_e8m0_golden():
+    for amax, byte in _read_golden("e8m0_ceil.txt"):
+        t = o.e8m0_ceil_exponent(np.array([float(amax)]))[0]
+        assert t + 127 == int(byte), amax
+
+
+def test_e8m0_bruteforce():
+    rng = np.random.default_rng(7)
+    a = np.concatenate([10.0 ** rng.uniform(-6, 4, 2000), 448.0 * 2.0 ** np.arange(-20, 20),
+                        np.nextafter(448.0 * 2.0 ** np.arange(-20, 20), np.inf),
+                        np.nextafter(448.0 * 2.0 ** np.arange(-20, 20), 0)])
+    got = o.e8m0_ceil_exponent(a)
+    assert [int(t) for t in got] == [_bf_exponent(float(v)) for v in a]
+
+
+def test_e8m0_value_and_nan():
+    v = o.e8m0_value(np.array([0, 127, 128, 254, 255]))
+    assert v[1] == 1.0 and v[2] == 2.0 and v[0] == 2.0 ** -127 and v[3] == 2.0 ** 127
+    assert np.isnan(v[4])
+
+
+def test_e8m0_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        o.e8m0_ceil_exponent(np.array([1e-45]))      # would need t < -127
+
+
+# ------------------------------------------------------------------ quantizer pins
+def test_ceil_invariant_on_workload_blocks():
+    """Every block: amax / s <= 448 and amax / (s/2) > 448 (the scale is minimal)."""
+    w = wl.workload(4)                                 # log-uniform per-token magnitudes
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((256, 2304)).astype(np.float32)
+    x *= np.power(10.0, rng.uniform(-2, 2, (256, 1))).astype(np.float32)
+    q, s = o.quantize_act_1x128(x)
+    amax = np.abs(x.astype(np.float64).reshape(256, 18, 128)).max(axis=2)
+    scale = 2.0 ** (s.T.astype(np.float64) - 127)
+    assert np.all(amax / scale <= 448.0)
+    assert np.all(amax / (scale / 2) > 448.0)
+    assert np.all(np.abs(o.decode_e4m3(q)) <= 448.0)
+    bw = wl.draw(wl.Workload("t", "contiguous", 1, 256, 512, "bf16", w.seed, m_per_group=[1]))["b"]
+    qb, sb = o.quantize_weight_128x128(bw)
+    amaxb = np.abs(bw.astype(np.float64).reshape(1, 2, 128, 4, 128)).max(axis=(2, 4))
+    sc = 2.0 ** (sb.astype(np.float64) - 127)
+    assert np.all(amaxb / sc <= 448.0) and np.all(amaxb / (sc / 2) > 448.0)
+
+
+def test_quantizers_bruteforce_tiny_ragged():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((5, 260)) * 10.0 ** rng.uniform(-3, 3, (5, 1))).astype(np.float32)
+    x[2, 128:256] = 0.0                                # an all-zero block
+    q, s = o.quantize_act_1x128(x)
+    bq, bs = _bf_quant_act(x)
+    assert np.array_equal(q, bq) and np.array_equal(s, bs)
+    w = rng.standard_normal((2, 130, 260)).astype(np.float32) * 3
+    qw, sw = o.quantize_weight_128x128(w)
+    bqw, bsw = _bf_quant_weight(w)
+    assert np.array_equal(qw, bqw) and np.array_equal(sw, bsw)
+
+
+def test_masked_quantizer_layout():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((3, 7, 256)).astype(np.float32)
+    q, s = o.quantize_act_masked(x)
+    assert q.shape == (3, 7, 256) and s.shape == (3, 2, 7)
+    for g in range(3):
+        qg, sg = _bf_quant_act(x[g])
+        assert np.array_equal(q[g], qg) and np.array_equal(s[g], sg)
+
+
+# ------------------------------------------------------------------ GEMM pins
+def test_contiguous_gemm_bruteforce_tiny():
+    rng = np.random.default_rng(11)
+    layout = np.array([0, 0, 0, -1, 1, 1, -1, -1, 1], np.int32)   # ragged, padding inside
+    K, N = 260, 130
+    a = rng.standard_normal((layout.size, K)).astype(np.float32)
+    b = rng.standard_normal((2, N, K)).astype(np.float32)
+    qa, sa = o.quantize_act_1x128(a)
+    qb, sb = o.quantize_weight_128x128(b)
+    d0 = np.full((layout.size, N), -7.0)
+    d = o.grouped_gemm_contiguous(qa, sa, qb, sb, layout, d0)
+    for g in range(2):
+        rows = [r for r in range(layout.size) if layout[r] == g]
+        ref = _bf_gemm_rows(qa, sa, qb, sb, rows, g)
+        np.testing.assert_allclose(d[rows], ref, rtol=1e-12, atol=1e-12)
+    assert np.all(d[layout < 0] == -7.0)
+
+
+def test_masked_gemm_bruteforce_tiny():
+    rng = np.random.default_rng(12)
+    G, Mmax, N, K = 3, 6, 130, 260
+    a = rng.standard_normal((G, Mmax, K)).astype(np.float32)
+    b = rng.standard_normal((G, N, K)).astype(np.float32)
+    masked_m = np.array([4, 0, 6], np.int32)
+    qa, sa = o.quantize_act_masked(a)
+    qb, sb = o.quantize_weight_128x128(b)
+    d0 = np.full((G, Mmax, N), 3.5)
+    d = o.grouped_gemm_masked(qa, sa, qb, sb, masked_m, d0)
+    for g in range(G):
+        mm = masked_m[g]
+        if mm:
+            ref = _bf_gemm_rows(qa[g], sa[g], qb, sb, list(range(mm)), g)
+            np.testing.assert_allclose(d[g, :mm], ref, rtol=1e-12, atol=1e-12)
+        assert np.all(d[g, mm:] == 3.5)
+
+
+def test_exact_integer_special_case():
+    """Integer FP8 inputs with scales 2^0..2^2: D equals the exact integer product."""
+    case = wl.integer_case(13, G=2, rows=5, N=256, K=384)
+    table = {int(i): int(c, 16) for i, c in _read_golden("e4m3_small_integers.txt")}
+    qa = np.vectorize(table.get)(case["ints_a"]).astype(np.uint8)
+    qb = np.vectorize(table.get)(case["ints_b"]).astype(np.uint8)
+    d = o.grouped_gemm_contiguous(qa, case["scale_a"], qb, case["scale_b"], case["grouped_layout"])
+    ia, ib = case["ints_a"], case["ints_b"]
+    sa = case["scale_a"].astype(np.int64) - 127
+    sb = case["scale_b"].astype(np.int64) - 127
+    for r in range(ia.shape[0]):
+        g = int(case["grouped_layout"][r])
+        for n in range(0, 256, 37):
+            exact = sum(int(ia[r, k]) * int(ib[g, n, k]) * 2 ** int(sa[k // 128, r] + sb[g, n // 128, k // 128])
+                        for k in range(384))
+            assert d[r, n] == exact
+
+
+def test_cross_layout_masked_equals_contiguous():
+    rng = np.random.default_rng(14)
+    counts = [5, 0, 9]
+    N, K, Mmax = 128, 256, 16
+    b = rng.standard_normal((3, N, K)).astype(np.float32)
+    a_m = rng.standard_normal((3, Mmax, K)).astype(np.float32)
+    layout = wl.contiguous_layout(counts, align=16)
+    a_c = np.zeros((layout.size, K), np.float32)
+    pos = 0
+    for g, c in enumerate(counts):
+        a_c[pos:pos + c] = a_m[g, :c]
+        pos += -(-c // 16) * 16
+    qb, sb = o.quantize_weight_128x128(b)
+    qa, sa = o.quantize_act_masked(a_m)
+    dm = o.grouped_gemm_masked(qa, sa, qb, sb, np.array(counts))
+    qc, sc = o.quantize_act_1x128(a_c)
+    dc = o.grouped_gemm_contiguous(qc, sc, qb, sb, layout)
+    pos = 0
+    for g, c in enumerate(counts):
+        assert np.array_equal(dm[g, :c], dc[pos:pos + c])
+        pos += -(-c // 16) * 16
+
+
+@pytest.mark.parametrize("idx,rows", [(0, None), (1, 256), (2, 300), (4, 256)])
+def test_fp32_product_bound(idx, rows):
+    """calc_diff(oracle, pre-quantization fp32 product) <= 1e-3 (page 1's threshold)."""
+    w = wl.workload(idx)
+    if rows is not None:                               # a slice of the workload's rows
+        w = wl.Workload(w.name, "contiguous", 2, w.N, w.K, w.out_dtype, w.seed,
+                        m_per_group=[rows // 2, rows - rows // 2], row_log10_range=w.row_log10_range)
+        w.N = min(w.N, 1024)
+    x = wl.draw(w)
+    qa, sa = o.quantize_act_1x128(x["a"])
+    qb, sb = o.quantize_weight_128x128(x["b"])
+    d = o.grouped_gemm_contiguous(qa, sa, qb, sb, x["grouped_layout"])
+    lay = x["grouped_layout"]
+    ref = np.full_like(d, np.nan)
+    for g in range(w.G):
+        rows_g = lay == g
+        ref[rows_g] = x["a"][rows_g].astype(np.float64) @ x["b"][g].astype(np.float64).T
+    valid = lay >= 0
+    diff = o.calc_diff(d[valid], ref[valid])
+    assert diff <= 1e-3, diff
+    assert diff > 1e-6                                  # quantization error is really present
+
+
+def test_calc_diff_closed_forms():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal(1000)
+    assert o.calc_diff(x, x) == pytest.approx(0.0, abs=1e-15)
+    assert o.calc_diff(x, -x) == pytest.approx(2.0)
+    assert o.calc_diff(x, 2 * x) == pytest.approx(0.2)              # 1 - 4/5
+    y = rng.standard_normal(1000)
+    assert o.calc_diff(x, y) == pytest.approx(np.sum((x - y) ** 2) / np.sum(x * x + y * y))
+
+
+def test_max_rel_err_rowfloor():
+    ref = np.array([[100.0, 1e-9, -50.0], [0.0, 0.0, 0.0]])
+    got = ref + np.array([[1.0, 0.05, 0.0], [0.0, 0.0, 0.0]])
+    # element (0,1): |0.05| / max(1e-9, 1e-3*100) = 0.5; element (0,0): 1/100
+    assert o.max_rel_err_rowfloor(got, ref) == pytest.approx(0.5)
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(16)
+    x = (rng.standard_normal(100000) * 10.0 ** rng.uniform(-5, 5, 100000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(o.round_to_bf16(x.astype(np.float64)), ref)
+
+
+def test_round_f16_matches_numpy():
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal(100000) * 10.0 ** rng.uniform(-6, 4, 100000))
+    x = x[np.abs(x) < 65504]
+    assert np.array_equal(o.round_to_f16(x), x.astype(np.float16).astype(np.float64))
+
+
+# ------------------------------------------------------------------ planted mistakes
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible mistakes in the oracle (on the CPU) and check a pin fails."""
+    failures = 0
+    # floor instead of ceil for the scale exponent
+    real = o.e8m0_ceil_exponent
+    monkeypatch.setattr(o, "e8m0_ceil_exponent",
+                        lambda a: np.where(np.asarray(a) > 0, np.floor(np.log2(np.where(np.asarray(a) > 0, a, 1) / 448)), 0).astype(np.int64))
+    try:
+        test_e8m0_golden()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "e8m0_ceil_exponent", real)
+    # weight scale read transposed (K-block index used as N-block index)
+    real_dw = o.dequantize_weight
+
+    def wrong_dw(q, scale):
+        return real_dw(q, np.ascontiguousarray(np.swapaxes(scale, 1, 2)) if scale.shape[1] == scale.shape[2] else scale[:, ::-1])
+    monkeypatch.setattr(o, "dequantize_weight", wrong_dw)
+    try:
+        test_contiguous_gemm_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "dequantize_weight", real_dw)
+    # B used untransposed-by-group: group index off by one
+    real_gc = o.grouped_gemm_contiguous
+
+    def wrong_gc(qa, sa, qb, sb, layout, d_init=None):
+        return real_gc(qa, sa, qb[::-1].copy(), sb[::-1].copy(), layout, d_init)
+    monkeypatch.setattr(o, "grouped_gemm_contiguous", wrong_gc)
+    try:
+        test_contiguous_gemm_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "grouped_gemm_contiguous", real_gc)
+    assert failures == 3
