@@ -1,1 +1,202 @@
-"""grouped FP8 block-scaled GEMM for MI355X."""
+"""Grouped FP8 (E4M3) block-scaled GEMM for MI355X (gfx950).
+
+A thin ctypes binding over ``libgfg.so`` (declared in ``include/gfg.h``):
+argument marshalling only.  Every step of the GEMM runs in the library's HIP
+kernels; the quantizers run in the library's C++ host code.  There is no
+fallback: if the library is missing or fails to load, every call raises.
+
+The operations are the two DeepGEMM-style grouped ops described on the first
+reference page, "Grouped and Batched GEMM kernels with blockscaling matching
+DeepGEMM API": a contiguous layout (``grouped_layout`` maps rows to experts,
+-1 marks padding) and a masked layout (``[G, M_max, K]`` with ``masked_m``),
+FP8 E4M3 operands with (1,128) activation and (128,128) weight E8M0 scales.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "GfgError", "load_library", "grouped_fp8_gemm_contiguous", "grouped_fp8_gemm_masked",
+    "fp8_quantize_act_1x128", "fp8_quantize_weight_128x128", "fp8_quantize_act_masked",
+    "raw_contiguous", "raw_masked", "OUT_BF16", "OUT_F16",
+]
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgfg.so")
+OUT_BF16, OUT_F16 = 0, 1
+_STATUS = {0: "GFG_OK", 1: "GFG_EINVAL", 2: "GFG_EUNSUPPORTED", 3: "GFG_EHIP", 4: "GFG_ERANGE"}
+_lib = None
+
+
+class GfgError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libgfg.so (once).  Raises if it is missing: there is no fallback path."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing; build it with `python -m fp8_block_scaled_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i64, i32, u8p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.grouped_fp8_gemm_contiguous.argtypes = [vp, u8p, vp, u8p, vp, vp, i64, i64, i64, i32, i32, vp]
+    lib.grouped_fp8_gemm_contiguous.restype = ctypes.c_int
+    lib.grouped_fp8_gemm_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
+    lib.grouped_fp8_gemm_masked.restype = ctypes.c_int
+    lib.fp8_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp]
+    lib.fp8_quantize_act_1x128.restype = ctypes.c_int
+    lib.fp8_quantize_weight_128x128.argtypes = [vp, i32, i64, i64, vp, vp]
+    lib.fp8_quantize_weight_128x128.restype = ctypes.c_int
+    lib.gfg_last_error.argtypes = []
+    lib.gfg_last_error.restype = ctypes.c_char_p
+    lib.gfg_version.argtypes = []
+    lib.gfg_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise GfgError(rc, load_library().gfg_last_error().decode())
+
+
+# ------------------------------------------------------------------ raw pointer calls
+def raw_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out_dtype, stream=0) -> int:
+    """Call the C entry point with integer addresses; returns the status code."""
+    return load_library().grouped_fp8_gemm_contiguous(a, a_scale, b, b_scale, grouped_layout, d,
+                                                      M, N, K, G, out_dtype, stream)
+
+
+def raw_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, stream=0) -> int:
+    return load_library().grouped_fp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d,
+                                                  G, M_max, N, K, out_dtype, stream)
+
+
+# ------------------------------------------------------------------ torch-facing calls
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name, dtypes, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.data_ptr()
+
+
+def _out_code(d):
+    torch = _torch()
+    if d.dtype == torch.bfloat16:
+        return OUT_BF16
+    if d.dtype == torch.float16:
+        return OUT_F16
+    raise TypeError(f"d has dtype {d.dtype}; expected bfloat16 or float16")
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def grouped_fp8_gemm_contiguous(a, a_scale, b, b_scale, grouped_layout, d, stream=None):
+    """D[rows of expert g] = A[rows] . B[g]^T on the GPU (asynchronous on ``stream``).
+
+    a [M, K] e4m3 (torch.float8_e4m3fn or uint8 codes), a_scale [ceil(K/128), M] uint8 E8M0,
+    b [G, N, K] e4m3, b_scale [G, ceil(N/128), ceil(K/128)] uint8, grouped_layout [M] int32,
+    d [M, N] bfloat16/float16 (padding rows untouched).  All on the same GPU, contiguous.
+    """
+    torch = _torch()
+    dev = d.device
+    f8 = (torch.uint8, torch.float8_e4m3fn)
+    M, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K or tuple(d.shape) != (M, N) or tuple(grouped_layout.shape) != (M,):
+        raise ValueError("shape mismatch between a, b, grouped_layout and d")
+    if tuple(a_scale.shape) != (-(-K // 128), M) or tuple(b_scale.shape) != (G, -(-N // 128), -(-K // 128)):
+        raise ValueError("scale tensor shapes do not match the (1,128)/(128,128) layouts")
+    _check(raw_contiguous(
+        _dev_ptr(a, "a", f8, dev), _dev_ptr(a_scale, "a_scale", (torch.uint8,), dev),
+        _dev_ptr(b, "b", f8, dev), _dev_ptr(b_scale, "b_scale", (torch.uint8,), dev),
+        _dev_ptr(grouped_layout, "grouped_layout", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev),
+        M, N, K, G, _out_code(d), _stream_handle(stream, dev)))
+    return d
+
+
+def grouped_fp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d, stream=None):
+    """D[g, m < masked_m[g]] = A[g, m] . B[g]^T on the GPU (asynchronous on ``stream``).
+
+    a [G, M_max, K] e4m3, a_scale [G, ceil(K/128), M_max] uint8, b [G, N, K], b_scale
+    [G, ceil(N/128), ceil(K/128)], masked_m [G] int32 (device), d [G, M_max, N].
+    """
+    torch = _torch()
+    dev = d.device
+    f8 = (torch.uint8, torch.float8_e4m3fn)
+    G, Mmax, K = a.shape
+    Gb, N, Kb = b.shape
+    if Gb != G or Kb != K or tuple(d.shape) != (G, Mmax, N) or tuple(masked_m.shape) != (G,):
+        raise ValueError("shape mismatch between a, b, masked_m and d")
+    if tuple(a_scale.shape) != (G, -(-K // 128), Mmax) or tuple(b_scale.shape) != (G, -(-N // 128), -(-K // 128)):
+        raise ValueError("scale tensor shapes do not match the (1,128)/(128,128) layouts")
+    _check(raw_masked(
+        _dev_ptr(a, "a", f8, dev), _dev_ptr(a_scale, "a_scale", (torch.uint8,), dev),
+        _dev_ptr(b, "b", f8, dev), _dev_ptr(b_scale, "b_scale", (torch.uint8,), dev),
+        _dev_ptr(masked_m, "masked_m", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev),
+        G, Mmax, N, K, _out_code(d), _stream_handle(stream, dev)))
+    return d
+
+
+# ------------------------------------------------------------------ host quantizers
+def _host_f32(x, name):
+    x = np.ascontiguousarray(np.asarray(x), dtype=np.float32)
+    return x
+
+
+def fp8_quantize_act_1x128(x):
+    """x [M, K] float32 (host) -> (q [M, K] uint8 e4m3, scale_t [ceil(K/128), M] uint8)."""
+    x = _host_f32(x, "x")
+    M, K = x.shape
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((-(-K // 128), M), np.uint8)
+    _check(load_library().fp8_quantize_act_1x128(x.ctypes.data, M, K, q.ctypes.data, s.ctypes.data))
+    return q, s
+
+
+def fp8_quantize_act_masked(x):
+    """x [G, M_max, K] float32 -> (q [G, M_max, K], scale_t [G, ceil(K/128), M_max])."""
+    x = _host_f32(x, "x")
+    G, Mmax, K = x.shape
+    q = np.empty((G, Mmax, K), np.uint8)
+    s = np.empty((G, -(-K // 128), Mmax), np.uint8)
+    lib = load_library()
+    for g in range(G):
+        _check(lib.fp8_quantize_act_1x128(x[g].ctypes.data, Mmax, K, q[g].ctypes.data, s[g].ctypes.data))
+    return q, s
+
+
+def fp8_quantize_weight_128x128(w):
+    """w [G, N, K] float32 (host) -> (q [G, N, K] uint8, scale [G, ceil(N/128), ceil(K/128)] uint8)."""
+    w = _host_f32(w, "w")
+    G, N, K = w.shape
+    q = np.empty((G, N, K), np.uint8)
+    s = np.empty((G, -(-N // 128), -(-K // 128)), np.uint8)
+    _check(load_library().fp8_quantize_weight_128x128(w.ctypes.data, G, N, K, q.ctypes.data, s.ctypes.data))
+    return q, s

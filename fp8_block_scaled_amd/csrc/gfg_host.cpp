@@ -1,0 +1,171 @@
+// Host side of libgfg: error reporting and the CPU quantizers.
+//
+// The quantizers produce the operands the GEMM consumes, as the first
+// reference page ("Grouped and Batched GEMM kernels with blockscaling
+// matching DeepGEMM API", section "DeepGEMM conformance details") describes:
+// E8M0 block scales rounded up to a power of two so that |x / scale| <= 448,
+// extracted on the host as plain bytes.  Per-token (1,128) blocks for
+// activations, stored transposed [ceil(K/128)][M]; (128,128) blocks for
+// weights.  E4M3 values are rounded to nearest, ties to even.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "gfg.h"
+#include "gfg_internal.h"
+
+namespace gfg {
+
+static thread_local std::string t_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    t_last_error = buf;
+    return code;
+}
+
+void clear_error() { t_last_error.clear(); }
+
+namespace {
+
+inline uint32_t f2u(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
+
+// Smallest integer t with 448 * 2^t >= amax, read off the float's bit fields.
+// amax = 1.f * 2^e; 448 = 1.75 * 2^8, so t = e - 8 when 1.f <= 1.75 (mantissa
+// field <= 0x600000) and e - 7 otherwise.  Subnormal amax go through frexp.
+// Returns false when t is outside the E8M0 range or amax is not finite.
+bool ceil_e8m0(float amax, int* t) {
+    if (!(amax >= 0.0f) || std::isinf(amax)) return false;
+    if (amax == 0.0f) { *t = 0; return true; }
+    uint32_t u = f2u(amax);
+    int e = int(u >> 23) - 127;
+    uint32_t mant = u & 0x7FFFFFu;
+    if (e == -127) {                       // subnormal: normalize by hand
+        int p;
+        float f = std::frexp(amax, &p);    // amax = f * 2^p, f in [0.5, 1)
+        uint32_t uf = f2u(f * 2.0f);       // 1.x in [1, 2)
+        e = p - 1;
+        mant = uf & 0x7FFFFFu;
+    }
+    int tt = (mant <= 0x600000u) ? e - 8 : e - 7;
+    if (tt < -127 || tt > 127) return false;
+    *t = tt;
+    return true;
+}
+
+// Nearest E4M3FN code of v (|v| <= 448), ties to the even mantissa.
+inline uint8_t e4m3_rne(float v) {
+    uint32_t u = f2u(v);
+    uint8_t sign = uint8_t((u >> 24) & 0x80u);
+    u &= 0x7FFFFFFFu;
+    float a;
+    std::memcpy(&a, &u, 4);
+    if (a < 0.015625f) {                   // below 2^-6: subnormal step 2^-9
+        int m = int(std::nearbyint(a * 512.0f));   // exact scaling; RNE
+        return uint8_t(sign | m);          // m == 8 is the smallest normal, code 0x08
+    }
+    int e = int(u >> 23) - 127;            // -6 .. 8
+    uint32_t mant = u & 0x7FFFFFu;
+    uint32_t r = mant >> 20, rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+    if (r == 8) { r = 0; ++e; }
+    return uint8_t(sign | uint8_t(((e + 7) << 3) | int(r)));
+}
+
+template <class F>
+void parallel_for(int64_t n, F&& f) {
+    unsigned hw = std::thread::hardware_concurrency();
+    int64_t nt = std::min<int64_t>({int64_t(hw ? hw : 1), int64_t(16), n});
+    if (nt <= 1) { for (int64_t i = 0; i < n; ++i) f(i); return; }
+    std::vector<std::thread> th;
+    for (int64_t w = 0; w < nt; ++w)
+        th.emplace_back([&, w] { for (int64_t i = w; i < n; i += nt) f(i); });
+    for (auto& t : th) t.join();
+}
+
+}  // namespace
+}  // namespace gfg
+
+using namespace gfg;
+
+extern "C" const char* gfg_last_error(void) { return t_last_error.c_str(); }
+
+extern "C" const char* gfg_version(void) { return "gfg 0.1 gfx950"; }
+
+extern "C" int fp8_quantize_act_1x128(const float* x, int64_t M, int64_t K,
+                                      uint8_t* q, uint8_t* scale_t) {
+    clear_error();
+    if (M < 0 || K <= 0) return fail(GFG_EINVAL, "fp8_quantize_act_1x128: bad sizes M=%lld K=%lld",
+                                    (long long)M, (long long)K);
+    if (M == 0) return GFG_OK;
+    if (!x || !q || !scale_t) return fail(GFG_EINVAL, "fp8_quantize_act_1x128: null pointer");
+    const int64_t KB = (K + 127) / 128;
+    std::vector<int> bad(size_t(M), 0);
+    parallel_for(M, [&](int64_t m) {
+        const float* row = x + m * K;
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            const int64_t k0 = kb * 128, k1 = std::min(K, k0 + 128);
+            float amax = 0.0f;
+            bool nan = false;
+            for (int64_t k = k0; k < k1; ++k) {
+                amax = std::max(amax, std::fabs(row[k]));
+                nan |= row[k] != row[k];
+            }
+            int t;
+            if (nan || !ceil_e8m0(amax, &t)) { bad[size_t(m)] = 1; return; }
+            scale_t[kb * M + m] = uint8_t(t + 127);
+            for (int64_t k = k0; k < k1; ++k) q[m * K + k] = e4m3_rne(std::ldexp(row[k], -t));
+        }
+    });
+    for (int64_t m = 0; m < M; ++m)
+        if (bad[size_t(m)])
+            return fail(GFG_ERANGE, "fp8_quantize_act_1x128: row %lld has a block outside the E8M0 range "
+                        "or a non-finite value", (long long)m);
+    return GFG_OK;
+}
+
+extern "C" int fp8_quantize_weight_128x128(const float* w, int32_t G, int64_t N, int64_t K,
+                                           uint8_t* q, uint8_t* scale) {
+    clear_error();
+    if (G <= 0 || N <= 0 || K <= 0)
+        return fail(GFG_EINVAL, "fp8_quantize_weight_128x128: bad sizes G=%d N=%lld K=%lld",
+                    G, (long long)N, (long long)K);
+    if (!w || !q || !scale) return fail(GFG_EINVAL, "fp8_quantize_weight_128x128: null pointer");
+    const int64_t NB = (N + 127) / 128, KB = (K + 127) / 128;
+    std::vector<int> bad(size_t(G * NB), 0);
+    parallel_for(int64_t(G) * NB, [&](int64_t gn) {
+        const int64_t g = gn / NB, nb = gn % NB;
+        const int64_t n0 = nb * 128, n1 = std::min(N, n0 + 128);
+        const float* wg = w + g * N * K;
+        uint8_t* qg = q + g * N * K;
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            const int64_t k0 = kb * 128, k1 = std::min(K, k0 + 128);
+            float amax = 0.0f;
+            bool nan = false;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int64_t k = k0; k < k1; ++k) {
+                    amax = std::max(amax, std::fabs(wg[n * K + k]));
+                    nan |= wg[n * K + k] != wg[n * K + k];
+                }
+            int t;
+            if (nan || !ceil_e8m0(amax, &t)) { bad[size_t(gn)] = 1; return; }
+            scale[(g * NB + nb) * KB + kb] = uint8_t(t + 127);
+            for (int64_t n = n0; n < n1; ++n)
+                for (int64_t k = k0; k < k1; ++k) qg[n * K + k] = e4m3_rne(std::ldexp(wg[n * K + k], -t));
+        }
+    });
+    for (int64_t i = 0; i < int64_t(G) * NB; ++i)
+        if (bad[size_t(i)])
+            return fail(GFG_ERANGE, "fp8_quantize_weight_128x128: block row %lld has a block outside the "
+                        "E8M0 range or a non-finite value", (long long)i);
+    return GFG_OK;
+}

@@ -1,0 +1,132 @@
+/*
+ * gfg.h — grouped FP8 (E4M3) block-scaled GEMM for MI355X (gfx950).
+ *
+ * C ABI of libgfg.so.  The operations are those of the first reference page,
+ * "Grouped and Batched GEMM kernels with blockscaling matching DeepGEMM API"
+ * (sections "Summary" and "DeepGEMM conformance details"):
+ *
+ *   D[rows of expert g] = A[rows] . B[g]^T          (contiguous layout)
+ *   D[g, m, :]          = A[g, m, :] . B[g]^T       (masked layout, m < masked_m[g])
+ *
+ * with FP8 E4M3FN operands, one E8M0 scale per (1,128) block of A (per token,
+ * per 128 channels, stored transposed as [ceil(K/128), M]) and one per
+ * (128,128) block of B.  An E8M0 byte b means the scale 2^(b-127); b = 255
+ * is NaN.  The product is exactly the product of the dequantized operands up
+ * to fp32 summation order; D is rounded once to bf16 or f16 (nearest even).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense, row-major, contiguous, with the last named axis
+ *    fastest.  "K-contiguous" ("nt"): A rows and B rows both run along K.
+ *  - GEMM tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or synchronizes inside a GEMM call; the
+ *    call is asynchronous on `stream` (a hipStream_t, NULL = null stream).
+ *  - Quantizer pointers are HOST pointers owned by the caller; the quantizers
+ *    are synchronous CPU functions.
+ *  - Return value: GFG_OK (0) or an error code; no exceptions cross the ABI.
+ *    gfg_last_error() returns a thread-local message for the last failure on
+ *    the calling thread (valid until that thread's next call).
+ *  - Argument checks (null pointers, sizes, enum values) happen on the host
+ *    before anything is launched.  Device-resident metadata cannot be
+ *    checked without a sync, so the kernels treat a grouped_layout entry
+ *    outside [0, G) as padding and clamp masked_m[g] into [0, M_max].
+ */
+#ifndef GFG_H
+#define GFG_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define GFG_API __attribute__((visibility("default")))
+#else
+#define GFG_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gfg_status {
+    GFG_OK = 0,
+    GFG_EINVAL = 1,       /* bad pointer, size or enum value                      */
+    GFG_EUNSUPPORTED = 2, /* valid for the method, outside what the kernels tile  */
+    GFG_EHIP = 3,         /* a HIP runtime call or kernel launch failed           */
+    GFG_ERANGE = 4        /* quantizer: a block scale falls outside E8M0's range  */
+};
+
+enum gfg_out_dtype { GFG_OUT_BF16 = 0, GFG_OUT_F16 = 1 };
+
+/*
+ * Contiguous grouped GEMM (the DeepGEMM-style m_grouped ... contiguous op).
+ *
+ *   a              [M][K]               e4m3 bytes
+ *   a_scale        [ceil(K/128)][M]     E8M0 bytes, per token per 128-K block (transposed)
+ *   b              [G][N][K]            e4m3 bytes
+ *   b_scale        [G][ceil(N/128)][ceil(K/128)]  E8M0 bytes, K-block fastest
+ *   grouped_layout [M]                  int32 expert id per row, -1 = padding
+ *   d              [M][N]               bf16 or f16, written for rows whose
+ *                                       grouped_layout is in [0, G); padding rows
+ *                                       are left untouched
+ *
+ * Layout precondition: each expert's rows form runs that start on a multiple
+ * of 128, padded with -1 up to the next multiple of 128, so every aligned
+ * 128-row tile belongs to one expert (the expert of its first row; a tile
+ * whose first row is padding is skipped).  A row whose entry differs from its
+ * tile's expert is left untouched.
+ *
+ * Sizes: M >= 0 (M = 0 is a no-op), N > 0 and K > 0 multiples of 128
+ * (else GFG_EUNSUPPORTED), 1 <= G <= 65535, ceil(M/128) <= 4096 (else
+ * GFG_EUNSUPPORTED).
+ */
+GFG_API int grouped_fp8_gemm_contiguous(const void* a, const uint8_t* a_scale,
+                                const void* b, const uint8_t* b_scale,
+                                const int32_t* grouped_layout, void* d,
+                                int64_t M, int64_t N, int64_t K, int32_t G,
+                                int32_t out_dtype, void* stream);
+
+/*
+ * Masked grouped GEMM (the DeepGEMM-style m_grouped ... masked op).
+ *
+ *   a         [G][M_max][K]               e4m3 bytes
+ *   a_scale   [G][ceil(K/128)][M_max]     E8M0 bytes (the transposed layout, per group)
+ *   b         [G][N][K]                   e4m3 bytes
+ *   b_scale   [G][ceil(N/128)][ceil(K/128)]
+ *   masked_m  [G]                         int32, DEVICE memory: rows computed per group
+ *   d         [G][M_max][N]               rows m < masked_m[g] written, others untouched
+ *
+ * Sizes: M_max >= 0, N and K positive multiples of 128, 1 <= G <= 65535,
+ * G * ceil(M_max/128) <= 4096 (else GFG_EUNSUPPORTED).
+ */
+GFG_API int grouped_fp8_gemm_masked(const void* a, const uint8_t* a_scale,
+                            const void* b, const uint8_t* b_scale,
+                            const int32_t* masked_m, void* d,
+                            int32_t G, int64_t M_max, int64_t N, int64_t K,
+                            int32_t out_dtype, void* stream);
+
+/*
+ * Host quantizers (CPU, synchronous), ceil-E8M0 scales and nearest-even E4M3:
+ * for each block, t = the smallest integer with 448 * 2^t >= amax (t = 0 for
+ * an all-zero block), scale byte = t + 127, q = E4M3(x / 2^t).  The rounding
+ * up of the scale is what keeps |x / scale| <= 448 (first reference page,
+ * section "DeepGEMM conformance details").  Ragged K (and N) are allowed:
+ * a partial block uses only its elements.  Returns GFG_ERANGE if a block
+ * needs t outside [-127, 127] or holds a non-finite value.
+ *
+ * fp8_quantize_act_1x128:    x [M][K] float -> q [M][K] e4m3, scale_t [ceil(K/128)][M]
+ * fp8_quantize_weight_128x128: w [G][N][K] float -> q [G][N][K], scale [G][ceil(N/128)][ceil(K/128)]
+ */
+GFG_API int fp8_quantize_act_1x128(const float* x, int64_t M, int64_t K,
+                           uint8_t* q, uint8_t* scale_t);
+GFG_API int fp8_quantize_weight_128x128(const float* w, int32_t G, int64_t N, int64_t K,
+                                uint8_t* q, uint8_t* scale);
+
+/* Thread-local message describing the calling thread's last failure ("" if none). */
+GFG_API const char* gfg_last_error(void);
+
+/* Library version string. */
+GFG_API const char* gfg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GFG_H */

@@ -1,0 +1,155 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol, its
+host quantizers are bit-exact with the oracle's, and its argument checks
+return the documented status codes before anything touches a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fp8_block_scaled_amd as gfg
+from fp8_block_scaled_amd import workloads as wl
+from oracle import fp8_oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", h)).read()
+            names += re.findall(r"GFG_API\s+[\w\s\*]+?\b(\w+)\s*\(", txt)
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gfg.load_library()
+    names = _declared_functions()
+    assert {"grouped_fp8_gemm_contiguous", "grouped_fp8_gemm_masked", "fp8_quantize_act_1x128",
+            "fp8_quantize_weight_128x128", "gfg_last_error", "gfg_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        gfg.load_library(str(tmp_path / "nope.so"))
+
+
+@pytest.mark.parametrize("shape", [(1, 128), (7, 260), (300, 1000), (64, 7168)])
+def test_act_quantizer_bit_exact(shape):
+    rng = np.random.default_rng(sum(shape))
+    x = (rng.standard_normal(shape) * 10.0 ** rng.uniform(-3, 3, (shape[0], 1))).astype(np.float32)
+    if shape[0] > 2:
+        x[1, :] = 0.0                         # all-zero blocks
+    q, s = gfg.fp8_quantize_act_1x128(x)
+    qo, so = o.quantize_act_1x128(x)
+    assert np.array_equal(q, qo) and np.array_equal(s, so)
+
+
+@pytest.mark.parametrize("shape", [(1, 128, 128), (2, 130, 260), (3, 384, 1000)])
+def test_weight_quantizer_bit_exact(shape):
+    rng = np.random.default_rng(sum(shape))
+    w = (rng.standard_normal(shape) * 3).astype(np.float32)
+    q, s = gfg.fp8_quantize_weight_128x128(w)
+    qo, so = o.quantize_weight_128x128(w)
+    assert np.array_equal(q, qo) and np.array_equal(s, so)
+
+
+def test_quantizers_bit_exact_on_workload_slices():
+    for idx in range(5):
+        w = wl.workload(idx)
+        x = wl.draw(wl.Workload(w.name, "contiguous", 1, 128, w.K, w.out_dtype, w.seed,
+                                m_per_group=[200], row_log10_range=w.row_log10_range))
+        q, s = gfg.fp8_quantize_act_1x128(x["a"])
+        qo, so = o.quantize_act_1x128(x["a"])
+        assert np.array_equal(q, qo) and np.array_equal(s, so)
+        qb, sb = gfg.fp8_quantize_weight_128x128(x["b"])
+        qbo, sbo = o.quantize_weight_128x128(x["b"])
+        assert np.array_equal(qb, qbo) and np.array_equal(sb, sbo)
+
+
+def test_quantizer_boundaries_bit_exact():
+    # amax exactly at and next to 448 * 2^t, every midpoint of the e4m3 grid
+    vals = np.array(sorted({float(v) for v in o.decode_e4m3(np.arange(0, 127, dtype=np.uint8))}))
+    mids = (vals[1:] + vals[:-1]) / 2
+    row = np.concatenate([vals, mids, -mids])
+    row = np.resize(row, 4 * 128).astype(np.float32)
+    x = np.stack([row, row * 2.0 ** -5, np.nextafter(row, np.float32(np.inf)).astype(np.float32)])
+    q, s = gfg.fp8_quantize_act_1x128(x)
+    qo, so = o.quantize_act_1x128(x)
+    assert np.array_equal(q, qo) and np.array_equal(s, so)
+
+
+def test_masked_quantizer_matches_oracle():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 50, 256)).astype(np.float32)
+    q, s = gfg.fp8_quantize_act_masked(x)
+    qo, so = o.quantize_act_masked(x)
+    assert np.array_equal(q, qo) and np.array_equal(s, so)
+
+
+def test_quantizer_range_errors():
+    with pytest.raises(gfg.GfgError) as e:
+        gfg.fp8_quantize_act_1x128(np.full((2, 128), np.nan, np.float32))
+    assert e.value.code == 4
+    with pytest.raises(gfg.GfgError) as e:
+        gfg.fp8_quantize_act_1x128(np.full((2, 128), 1e-44, np.float32))   # scale below 2^-127
+    assert e.value.code == 4
+    with pytest.raises(gfg.GfgError) as e:
+        gfg.fp8_quantize_weight_128x128(np.full((1, 128, 128), np.inf, np.float32))
+    assert e.value.code == 4
+
+
+def test_quantizer_argument_errors():
+    lib = gfg.load_library()
+    assert lib.fp8_quantize_act_1x128(None, 4, 128, None, None) == 1
+    assert lib.fp8_quantize_act_1x128(None, -1, 128, None, None) == 1
+    assert lib.fp8_quantize_act_1x128(None, 0, 128, None, None) == 0      # empty: no-op
+    assert lib.fp8_quantize_weight_128x128(None, 0, 128, 128, None, None) == 1
+
+
+# Host-side argument checks of the GEMM entry points: these return before any
+# HIP call, so fake non-null addresses are never dereferenced.
+FAKE = 0x1000
+
+
+def _c(**kw):
+    args = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, meta=FAKE, d=FAKE, M=256, N=256, K=256, G=2, dt=0)
+    args.update(kw)
+    return gfg.raw_contiguous(args["a"], args["sa"], args["b"], args["sb"], args["meta"], args["d"],
+                              args["M"], args["N"], args["K"], args["G"], args["dt"], 0)
+
+
+def _m(**kw):
+    args = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, meta=FAKE, d=FAKE, G=2, Mmax=256, N=256, K=256, dt=0)
+    args.update(kw)
+    return gfg.raw_masked(args["a"], args["sa"], args["b"], args["sb"], args["meta"], args["d"],
+                          args["G"], args["Mmax"], args["N"], args["K"], args["dt"], 0)
+
+
+@pytest.mark.parametrize("fn", [_c, _m])
+def test_gemm_argument_errors(fn):
+    for k in ("a", "sa", "b", "sb", "meta", "d"):
+        assert fn(**{k: None}) == 1, k
+    assert fn(dt=2) == 1
+    assert fn(G=0) == 1
+    assert fn(G=70000) == 1
+    assert fn(N=0) == 1
+    assert fn(K=-128) == 1
+    assert fn(N=200) == 2          # ragged N: outside the kernels' tiling
+    assert fn(K=300) == 2
+    msg = gfg.load_library().gfg_last_error().decode()
+    assert "multiples of 128" in msg
+
+
+def test_gemm_empty_and_oversize():
+    assert _c(M=0) == 0            # empty: no launch
+    assert _m(Mmax=0) == 0
+    assert _c(M=-1) == 1
+    assert _m(Mmax=-5) == 1
+    assert _c(M=4096 * 128 + 1) == 2
+    assert _m(G=33, Mmax=128 * 128) == 2
