@@ -1,0 +1,210 @@
+"""Benchmark: grouped FP8 block-scaled GEMM throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one call of the grouped GEMM (tile scheduling, LDS-staged scaled-MFMA
+K-loop and epilogue, all inside the one kernel) over one batch of seeded
+synthetic inputs already resident in HBM; quantization happens before timing,
+as the inputs of the op are FP8 bytes and E8M0 scales.  Several input sets
+whose combined size exceeds the 256 MB Infinity Cache rotate between steps, so
+each step streams its operands from HBM.
+
+Prints one JSON line: valid-row TFLOP/s (2 * M_valid * N * K / t), the
+roofline object for the kernel (HIP events on the launch stream), and the CPU
+oracle timed on the host cores on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA peak
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "contig_g4_m1024_n2048_k7168"
+KERNEL_SRC = os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", "gfg_gemm.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w, layout=None) -> int:
+    """Bytes the op must move at least once: A rows of non-empty tiles, B of the
+    experts that have rows, both scale tensors' used parts, and D's valid rows."""
+    KB, NB = w.K // 128, w.N // 128
+    out_b = 2
+    if w.layout == "masked":
+        tiles_rows = sum(-(-min(max(m, 0), w.M_max) // 128) * 128 for m in w.masked_m)
+        a_rows = sum(min(max(m, 0), w.M_max) for m in w.masked_m)
+        groups = sum(1 for m in w.masked_m if m > 0)
+    else:
+        tiles_rows = w.M
+        a_rows = w.M
+        groups = sum(1 for m in w.m_per_group if m > 0)
+    return int(a_rows * w.K + tiles_rows * KB + groups * (w.N * w.K + NB * KB)
+               + w.m_valid * w.N * out_b)
+
+
+def traffic_from_profile(w):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x):
+    """The fp64 oracle (dequantize, then matmul) on the same workload, timed on
+    the host.  Its own quantizer prepares the operands outside the timing."""
+    from threadpoolctl import threadpool_info
+    from oracle import fp8_oracle as o
+    if w.layout == "masked":
+        qa, sa = o.quantize_act_masked(x["a"])
+        qb, sb = o.quantize_weight_128x128(x["b"])
+        t0 = time.perf_counter()
+        o.grouped_gemm_masked(qa, sa, qb, sb, w.masked_m)
+        dt = time.perf_counter() - t0
+    else:
+        qa, sa = o.quantize_act_1x128(x["a"])
+        qb, sb = o.quantize_weight_128x128(x["b"])
+        t0 = time.perf_counter()
+        o.grouped_gemm_contiguous(qa, sa, qb, sb, x["grouped_layout"])
+        dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(w.flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one full step of {w.name} (fp64 dequantize + matmul over all valid rows), "
+                      f"{dt:.2f} s; quantization untimed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 256 MB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the grouped GEMM has no "
+                                   "multi-GPU path here (experts would be sharded across GPUs with "
+                                   "an all-to-all token exchange around the unchanged kernel)"}))
+        sys.exit(2)
+
+    import torch
+    import fp8_block_scaled_amd as gfg
+    from fp8_block_scaled_amd import workloads as wl
+
+    gfg.load_library()
+    w = wl.workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    per_set = algorithmic_bytes(w)
+    nsets = args.sets or max(2, -(-(300 << 20) // per_set))
+    sets = []
+    x0 = None
+    for s in range(nsets):
+        x = wl.draw(w, seed_offset=s)
+        if s == 0:
+            x0 = x
+        if w.layout == "masked":
+            qa, sa = gfg.fp8_quantize_act_masked(x["a"])
+            meta = torch.from_numpy(np.asarray(w.masked_m, np.int32)).to(dev)
+            M_rows = w.G * w.M_max
+        else:
+            qa, sa = gfg.fp8_quantize_act_1x128(x["a"])
+            meta = torch.from_numpy(x["grouped_layout"]).to(dev)
+            M_rows = w.M
+        qb, sb = gfg.fp8_quantize_weight_128x128(x["b"])
+        t = dict(a=torch.from_numpy(qa).to(dev), sa=torch.from_numpy(sa).to(dev),
+                 b=torch.from_numpy(qb).to(dev), sb=torch.from_numpy(sb).to(dev), meta=meta,
+                 d=torch.empty((M_rows, w.N), dtype=torch.bfloat16 if w.out_dtype == "bf16" else torch.float16,
+                               device=dev))
+        sets.append(t)
+        if s:
+            del x
+    out_code = gfg.OUT_BF16 if w.out_dtype == "bf16" else gfg.OUT_F16
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+
+    # prepared launches: pointers and sizes resolved once
+    calls = []
+    for t in sets:
+        if w.layout == "masked":
+            a = (t["a"].data_ptr(), t["sa"].data_ptr(), t["b"].data_ptr(), t["sb"].data_ptr(),
+                 t["meta"].data_ptr(), t["d"].data_ptr(), w.G, w.M_max, w.N, w.K, out_code, handle)
+            calls.append((gfg.raw_masked, a))
+        else:
+            a = (t["a"].data_ptr(), t["sa"].data_ptr(), t["b"].data_ptr(), t["sb"].data_ptr(),
+                 t["meta"].data_ptr(), t["d"].data_ptr(), w.M, w.N, w.K, w.G, out_code, handle)
+            calls.append((gfg.raw_contiguous, a))
+
+    def step(i):
+        fn, a = calls[i % len(calls)]
+        rc = fn(*a)
+        if rc:
+            raise gfg.GfgError(rc, gfg.load_library().gfg_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(w)
+
+    res = {
+        "metric": "grouped FP8 GEMM TFLOP/s (valid rows) and % of FP8 MFMA peak, 1 MI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layout": w.layout, "G": w.G, "N": w.N, "K": w.K,
+                   "M_rows": w.M, "M_valid": w.m_valid, "out": w.out_dtype,
+                   "input_sets": nsets, "parallelism": "none (1 GPU)"},
+        "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic},
+        "algorithmic_bytes_per_step": algorithmic_bytes(w),
+        "algorithmic_GBps": round(algorithmic_bytes(w) / (ms * 1e-3) / 1e9, 1),
+        "host_wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, x0)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
