@@ -60,6 +60,10 @@ struct Params {
 };
 
 // Byte offset of 16-byte chunk c (0..7) of row r inside a [rows][128 B] LDS tile.
+// XORing the chunk with r & 7 makes both access patterns conflict-free on
+// gfx950 (measured with SQ_LDS_BANK_CONFLICT): the MFMA fragment read (16
+// consecutive rows, one 16-byte chunk per lane) and the staging write (8 lanes
+// per row covering its 8 chunks).
 __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
 
 template <bool MASKED>
@@ -77,41 +81,236 @@ __device__ __forceinline__ bool cand_valid(const Params& p, int c, int* g_out) {
     }
 }
 
+#define GFG_LDS __attribute__((address_space(3)))
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most VM vector-memory
+// loads and LG LDS/scalar operations of this wave are outstanding.
+#define GFG_WAITCNT(VM, LG) \
+    __builtin_amdgcn_s_waitcnt(((VM) & 15) | ((((VM) >> 4) & 3) << 14) | (7 << 4) | (((LG) & 15) << 8))
+
+// Raw buffer resource over [base, base + bytes): stride 0, 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+
+// A wave-uniform pointer re-materialized from scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
+}
+
+// Per-tile, per-lane constants of the K loop.
+template <int BN>
+struct TileCtx {
+    static constexpr int WAVES = NTHREADS / 64;
+    static constexpr int WN = BN / 2;               // columns per wave (2 x 2 wave grid)
+    static constexpr int FN = WN / 16;              // 16-column MFMA tiles per wave
+    static constexpr int FM = 4;                    // 16-row MFMA tiles per wave (64 rows)
+    static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_DMA = A_BYTES / 1024 / WAVES;   // 1 KB LDS-DMA wave instructions per stage
+    static constexpr int B_DMA = B_BYTES / 1024 / WAVES;
+    // vector-memory loads one wave issues per stage: DMAs plus FM + 1 scale bytes
+    static constexpr int LOADS = A_DMA + B_DMA + FM + 1;
+
+    // Buffer resources (scalar registers): base + byte count.  The hardware
+    // returns zero for any offset past the count instead of touching memory.
+    const uint8_t* a_tile;            // A row m0, K 0 of the region
+    const uint8_t* b_tile;            // B row n0 of expert g, K 0
+    __amdgpu_buffer_rsrc_t sa_rsrc;   // scale_a from row m0 of K-block 0 to the region's end
+    __amdgpu_buffer_rsrc_t sb_rsrc;   // scale_b row of this wave's 128-column block
+    uint32_t sa_stride;        // scale_a bytes between K-blocks (rows of the region)
+    uint32_t a_off[A_DMA];     // per-lane source offsets of this wave's DMA chunks
+    uint32_t b_off[B_DMA];
+    uint32_t sa_off[TileCtx::FM];
+    // LDS byte offsets of this lane's fragment row, logical chunks lq (lo) and
+    // lq + 4 (hi); with the XOR swizzle the hi chunk sits at lo ^ 64.
+    int a_lo, a_hi, b_lo, b_hi;
+};
+
+template <int BN>
+struct Frags {
+    v8i a[4];
+    v8i b[BN / 32];
+};
+
+// Issue stage kb's loads: its A/B tiles by LDS DMA into buffer `dst` (laid out
+// with swz()) and this lane's scale bytes into (sa, sb).
+template <int BN>
+__device__ __forceinline__ void issue_stage(const TileCtx<BN>& c, GFG_LDS uint8_t* __restrict__ dst,
+                                            int kb, int wave, int (&sa)[4], int& sb) {
+    using C = TileCtx<BN>;
+    const uint32_t so = uint32_t(kb) * c.sa_stride;
+#pragma unroll
+    for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(c.sa_rsrc, c.sa_off[f], so, 0);
+    sb = __builtin_amdgcn_raw_buffer_load_b8(c.sb_rsrc, 0, kb, 0);
+    // K-block base pointers made opaque scalars, so each DMA address is a scalar
+    // base plus this lane's 32-bit offset (no per-lane 64-bit induction variables)
+    const uint8_t* ak = uniform_ptr(c.a_tile + int64_t(kb) * BK);
+    const uint8_t* bk = uniform_ptr(c.b_tile + int64_t(kb) * BK);
+#pragma unroll
+    for (int j = 0; j < C::A_DMA; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(ak + c.a_off[j]),
+                                         (GFG_LDS void*)(dst + (j * C::WAVES + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::B_DMA; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(bk + c.b_off[j]),
+                                         (GFG_LDS void*)(dst + C::A_BYTES + (j * C::WAVES + wave) * 1024), 16, 0, 0);
+}
+
+// Read this lane's fragments of one stage from LDS.  A fragment (16 rows x 128 K):
+// lane (l16, lq) holds row l16's 16-byte chunks lq and lq + 4.
+template <int BN>
+__device__ __forceinline__ void read_frags(const TileCtx<BN>& c, const GFG_LDS uint8_t* __restrict__ src,
+                                           Frags<BN>& f) {
+    using C = TileCtx<BN>;
+#pragma unroll
+    for (int y = 0; y < C::FM; ++y) {
+        const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + c.a_lo + y * 16 * BK);
+        const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + c.a_hi + y * 16 * BK);
+        f.a[y] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int x = 0; x < C::FN; ++x) {
+        const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + C::A_BYTES + c.b_lo + x * 16 * BK);
+        const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + C::A_BYTES + c.b_hi + x * 16 * BK);
+        f.b[x] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+
+template <int BN>
+__device__ __forceinline__ void mfma_stage(const Frags<BN>& f, const int (&sa)[4], int sb,
+                                           v4f (&acc)[TileCtx<BN>::FN][4]) {
+#pragma unroll
+    for (int x = 0; x < TileCtx<BN>::FN; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[x], f.a[y], acc[x][y], 0, 0, 0,
+                                                                         sb, 0, sa[y]);
+}
+
+// One K-step k.  On entry: fragments of stage k are in `cur` (their LDS reads
+// issued during step k-1), stage k+1's DMA was issued two steps ago.  The step
+// waits for its own stage-(k+1) DMA and for `cur`, meets the other waves at
+// the barrier (after which stage k+1 is visible and nobody reads stage k's
+// buffer any more), refills that buffer with stage k+3, issues the reads of
+// stage k+1's fragments, and runs stage k's MFMAs while those reads fly.
+// VMWAIT = vector-memory loads this wave issued after stage k+1's DMA.
+// Instruction order of one K-step for the scheduler: MFMA i is followed by
+// DMA i (while i < NV) and fragment read i (while i < NR), so the loads of
+// later stages are spread across this stage's MFMAs; the NS scale loads go last.
+template <int I, int NM, int NV, int NR, int NS>
+__device__ __forceinline__ void sched_pattern() {
+    if constexpr (I < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        if constexpr (I < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read (DMA)
+        if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        sched_pattern<I + 1, NM, NV, NR, NS>();
+    } else if constexpr (NS > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x020, NS, 0);           // scale loads
+    }
+}
+
+template <int BN, bool ISSUE, bool READ, int VMWAIT>
+__device__ __forceinline__ void k_step(const TileCtx<BN>& c, GFG_LDS uint8_t* __restrict__ refill,
+                                       const GFG_LDS uint8_t* __restrict__ next, int kb_refill, int wave,
+                                       Frags<BN>& cur, Frags<BN>& nxt, int (&sa)[4], int& sb,
+                                       v4f (&acc)[TileCtx<BN>::FN][4]) {
+    using C = TileCtx<BN>;
+    __builtin_amdgcn_sched_barrier(0);
+    GFG_WAITCNT(VMWAIT, 0);
+    __builtin_amdgcn_s_barrier();
+    int sa_use[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) sa_use[y] = sa[y];
+    const int sb_use = sb;
+    // The LDS DMA and the fragment reads are issued here, through this
+    // function's restrict parameters, so the compiler knows the refilled
+    // buffer and the buffer being read do not overlap and adds no wait for
+    // the DMA before the reads.
+    if (ISSUE) {
+        const uint8_t* ak = uniform_ptr(c.a_tile + int64_t(kb_refill) * BK);
+        const uint8_t* bk = uniform_ptr(c.b_tile + int64_t(kb_refill) * BK);
+#pragma unroll
+        for (int j = 0; j < C::A_DMA; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(ak + c.a_off[j]),
+                                             (GFG_LDS void*)(refill + (j * C::WAVES + wave) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::B_DMA; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(bk + c.b_off[j]),
+                                             (GFG_LDS void*)(refill + C::A_BYTES + (j * C::WAVES + wave) * 1024),
+                                             16, 0, 0);
+    }
+    if (READ) {
+#pragma unroll
+        for (int y = 0; y < C::FM; ++y) {
+            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + c.a_lo + y * 16 * BK);
+            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + c.a_hi + y * 16 * BK);
+            nxt.a[y] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int x = 0; x < C::FN; ++x) {
+            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + c.b_lo + x * 16 * BK);
+            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + c.b_hi + x * 16 * BK);
+            nxt.b[x] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    }
+    mfma_stage<BN>(cur, sa_use, sb_use, acc);
+    if (ISSUE) {   // after the MFMAs that read the old scale registers
+        const uint32_t so = uint32_t(kb_refill) * c.sa_stride;
+#pragma unroll
+        for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(c.sa_rsrc, c.sa_off[f], so, 0);
+        sb = __builtin_amdgcn_raw_buffer_load_b8(c.sb_rsrc, 0, kb_refill, 0);
+    }
+    sched_pattern<0, C::FN * C::FM, ISSUE ? C::A_DMA + C::B_DMA : 0, READ ? 2 * (C::FM + C::FN) : 0,
+                  ISSUE ? C::FM + 1 : 0>();
+    if (READ) cur = nxt;
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int BN, bool MASKED, typename OutT>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p) {
-    constexpr int WN = BN / 2;          // columns per wave (2 x 2 wave grid)
-    constexpr int FN = WN / 16;         // 16-column MFMA tiles per wave
-    constexpr int FM = 4;               // 16-row MFMA tiles per wave (64 rows)
-    constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
-    constexpr int A_LD = A_BYTES / (16 * NTHREADS);   // 16-byte loads per thread per step
-    constexpr int B_LD = B_BYTES / (16 * NTHREADS);
+    using C = TileCtx<BN>;
+    constexpr int FN = C::FN, FM = C::FM, WN = C::WN;
+    constexpr int L = C::LOADS;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_BYTES + B_BYTES)];
-    __shared__ int tile_list[MT_MAX];   // valid candidates, ascending: cand | group << 13
+    // three stage buffers as distinct LDS objects: the compiler gives each its
+    // own alias scope, so a DMA into one buffer does not make reads of another
+    // wait for it
+    __shared__ __attribute__((aligned(1024))) uint8_t smem0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem2[C::STAGE];
+    __shared__ uint16_t tile_list[MT_MAX];   // valid candidate 128-row tiles, ascending
     __shared__ int wave_count[NTHREADS / 64];
     __shared__ int s_total;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
 
     // ---- 1. compact the valid 128-row tiles (order preserved) --------------
     if (tid == 0) s_total = 0;
     __syncthreads();
     for (int base = 0; base < p.n_cand; base += NTHREADS) {
-        const int c = base + tid;
+        const int cnd = base + tid;
         int g = -1;
-        const bool v = c < p.n_cand && cand_valid<MASKED>(p, c, &g);
+        const bool v = cnd < p.n_cand && cand_valid<MASKED>(p, cnd, &g);
         const uint64_t bal = __ballot(v);
         const int before = __popcll(bal & ((uint64_t(1) << lane) - 1));
         if (lane == 0) wave_count[wave] = __popcll(bal);
         __syncthreads();
         int off = s_total;
         for (int w = 0; w < wave; ++w) off += wave_count[w];
-        if (v) tile_list[off + before] = c | (g << 13);
+        if (v) tile_list[off + before] = uint16_t(cnd);
         __syncthreads();
-        if (tid == 0) s_total += wave_count[0] + wave_count[1] + wave_count[2] + wave_count[3];
+        if (tid == 0) {
+            int sum = 0;
+            for (int w = 0; w < NTHREADS / 64; ++w) sum += wave_count[w];
+            s_total += sum;
+        }
         __syncthreads();
     }
-    const int n_mtiles = s_total;
+    const int n_mtiles = __builtin_amdgcn_readfirstlane(s_total);
     const int NT = p.N / BN;
     const unsigned T = unsigned(n_mtiles) * unsigned(NT);
 
@@ -126,6 +325,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
     const int NB = p.N / 128;
     const int wm = wave & 1, wn = wave >> 1;
     const int l16 = lane & 15, lq = lane >> 4;
+    GFG_LDS uint8_t* const buf0 = (GFG_LDS uint8_t*)smem0;
+    GFG_LDS uint8_t* const buf1 = (GFG_LDS uint8_t*)smem1;
+    GFG_LDS uint8_t* const buf2 = (GFG_LDS uint8_t*)smem2;
 
     for (unsigned i = slot; i < x_count; i += slots) {
         // grouped-M order over (valid m-tile rank, n-tile)
@@ -139,14 +341,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         const int r_rank = int(first + in_grp % gsz);
         const int nt = int(in_grp / gsz);
 
-        const int packed = tile_list[r_rank];
-        const int cand = packed & 8191, g = packed >> 13;
+        const int cand = __builtin_amdgcn_readfirstlane(int(tile_list[r_rank]));
+        int g;
         int64_t m0;             // first row of the tile inside its region
         const uint8_t* a_reg;   // region base (rows x K)
         const uint8_t* sa_reg;  // region's scale base ([KB][rows])
         uint8_t* d_reg;
         int mlimit;             // rows that may be computed
         if (MASKED) {
+            g = cand / p.mt_per_group;
             m0 = int64_t(cand - g * p.mt_per_group) * BM;
             a_reg = p.a + int64_t(g) * p.rows * p.K;
             sa_reg = p.a_scale + int64_t(g) * KB * p.rows;
@@ -155,43 +358,47 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             mlimit = mm < 0 ? 0 : (mm > p.rows ? int(p.rows) : mm);
         } else {
             m0 = int64_t(cand) * BM;
+            g = __builtin_amdgcn_readfirstlane(p.meta[m0]);
             a_reg = p.a;
             sa_reg = p.a_scale;
             d_reg = reinterpret_cast<uint8_t*>(p.d);
             mlimit = int(p.rows);
         }
         const int n0 = nt * BN;
-        const uint8_t* b_reg = p.b + (int64_t(g) * p.N + n0) * p.K;
 
-        // global source pointers for this thread's staging chunks
-        const uint8_t* pa[A_LD];
-        int a_lds[A_LD];
+        TileCtx<BN> c;
+        c.a_tile = a_reg + m0 * p.K;
+        c.b_tile = p.b + (int64_t(g) * p.N + n0) * p.K;
+        c.sa_rsrc = make_rsrc(sa_reg + m0, uint32_t(int64_t(KB) * p.rows - m0));
+        c.sb_rsrc = make_rsrc(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB, uint32_t(KB));
+        c.sa_stride = uint32_t(p.rows);
+        // DMA chunk j of this wave fills LDS rows 8*(j*WAVES + wave) .. +7; lane i
+        // writes physical chunk i%8 of row +i/8, which holds logical chunk
+        // (i%8) ^ (row & 7) of that row.
+        {
+            const int rr = lane >> 3, pc = lane & 7, lc = pc ^ rr;   // (row & 7) == rr
 #pragma unroll
-        for (int j = 0; j < A_LD; ++j) {
-            const int q = j * NTHREADS + tid, r = q >> 3, c = q & 7;
-            int64_t row = m0 + r;
-            row = row < mlimit ? row : (mlimit > 0 ? mlimit - 1 : 0);   // clamp: never read outside
-            pa[j] = a_reg + row * p.K + c * 16;
-            a_lds[j] = swz(r, c);
-        }
-        // B rows are all in bounds: chunk j of this thread is row j*32 + tid/8
-        const uint8_t* pb = b_reg + int64_t(tid >> 3) * p.K + (tid & 7) * 16;
-        const int64_t b_step = int64_t(NTHREADS / 8) * p.K;
-        int b_lds[B_LD];
+            for (int j = 0; j < C::A_DMA; ++j) {
+                int64_t row = m0 + 8 * (j * C::WAVES + wave) + rr;
+                row = row < mlimit ? row : mlimit - 1;           // clamp: never read outside
+                c.a_off[j] = uint32_t(row - m0) * uint32_t(p.K) + uint32_t(lc * 16);
+            }
 #pragma unroll
-        for (int j = 0; j < B_LD; ++j) {
-            const int q = j * NTHREADS + tid, r = q >> 3, c = q & 7;
-            b_lds[j] = swz(r, c);
+            for (int j = 0; j < C::B_DMA; ++j)
+                c.b_off[j] = uint32_t(8 * (j * C::WAVES + wave) + rr) * uint32_t(p.K) + uint32_t(lc * 16);
         }
-        // scale sources: this lane's 4 A rows, and the wave's B block row
-        const uint8_t* psa[FM];
 #pragma unroll
         for (int f = 0; f < FM; ++f) {
             int64_t row = m0 + wm * 64 + f * 16 + l16;
-            row = row < mlimit ? row : (mlimit > 0 ? mlimit - 1 : 0);
-            psa[f] = sa_reg + row;
+            row = row < mlimit ? row : mlimit - 1;
+            c.sa_off[f] = uint32_t(row - m0);
         }
-        const uint8_t* psb = p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB;
+        // fragment rows: A row wm*64 + y*16 + l16, B row wn*WN + x*16 + l16; the
+        // swizzle term (row & 7) == (l16 & 7) for all y, x.
+        c.a_lo = swz(wm * 64 + l16, lq);
+        c.a_hi = swz(wm * 64 + l16, lq + 4);
+        c.b_lo = swz(wn * WN + l16, lq);
+        c.b_hi = swz(wn * WN + l16, lq + 4);
 
         v4f acc[FN][FM];
 #pragma unroll
@@ -199,77 +406,58 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
 #pragma unroll
             for (int y = 0; y < FM; ++y) acc[x][y] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        u32x4 ra[A_LD], rb[B_LD];
-        int sa_cur[FM], sa_nxt[FM], sb_cur, sb_nxt;
+        Frags<BN> fa, fb;
+        int sa0[4], sa1[4], sa2[4], sb0 = 0, sb1 = 0, sb2 = 0;
 
-#define GFG_LOAD_STAGE(KBI)                                                                      \
-        {                                                                                        \
-            const int64_t ko_ = int64_t(KBI) * BK;                                               \
-            _Pragma("unroll") for (int j = 0; j < A_LD; ++j)                                     \
-                ra[j] = *reinterpret_cast<const u32x4*>(pa[j] + ko_);                  \
-            _Pragma("unroll") for (int j = 0; j < B_LD; ++j)                                     \
-                rb[j] = *reinterpret_cast<const u32x4*>(pb + j * b_step + ko_);                  \
+        // prologue: stages 0..2 in flight, stage 0's fragments in `fa`
+        issue_stage<BN>(c, buf0, 0, wave, sa0, sb0);
+        if (KB >= 3) {
+            issue_stage<BN>(c, buf1, 1, wave, sa1, sb1);
+            issue_stage<BN>(c, buf2, 2, wave, sa2, sb2);
+            GFG_WAITCNT(2 * L, 15);
+        } else if (KB == 2) {
+            issue_stage<BN>(c, buf1, 1, wave, sa1, sb1);
+            GFG_WAITCNT(L, 15);
+        } else {
+            GFG_WAITCNT(0, 15);
         }
-#define GFG_LOAD_SCALES(KBI, SA, SB)                                                             \
-        {                                                                                        \
-            _Pragma("unroll") for (int f = 0; f < FM; ++f) SA[f] = psa[f][int64_t(KBI) * p.rows]; \
-            SB = psb[KBI];                                                                       \
-        }
-#define GFG_STORE_STAGE(BUF)                                                                     \
-        {                                                                                        \
-            uint8_t* sA_ = smem + (BUF) * (A_BYTES + B_BYTES);                                   \
-            uint8_t* sB_ = sA_ + A_BYTES;                                                        \
-            _Pragma("unroll") for (int j = 0; j < A_LD; ++j)                                     \
-                *reinterpret_cast<u32x4*>(sA_ + a_lds[j]) = ra[j];                               \
-            _Pragma("unroll") for (int j = 0; j < B_LD; ++j)                                     \
-                *reinterpret_cast<u32x4*>(sB_ + b_lds[j]) = rb[j];                               \
-        }
+        __builtin_amdgcn_s_barrier();
+        read_frags<BN>(c, buf0, fa);
 
-        GFG_LOAD_STAGE(0)
-        GFG_LOAD_SCALES(0, sa_cur, sb_cur)
-        GFG_STORE_STAGE(0)
-        __syncthreads();
-
-        for (int kb = 0; kb < KB; ++kb) {
-            const int buf = kb & 1;
-            const bool more = kb + 1 < KB;
-            if (more) {
-                GFG_LOAD_STAGE(kb + 1)
-                GFG_LOAD_SCALES(kb + 1, sa_nxt, sb_nxt)
-            }
-            const uint8_t* sA = smem + buf * (A_BYTES + B_BYTES);
-            const uint8_t* sB = sA + A_BYTES;
-            // A fragments: lane (l16, lq) holds row l16 of the 16-row tile, chunks lq and lq+4
-            v8i af[FM];
-#pragma unroll
-            for (int f = 0; f < FM; ++f) {
-                const int r = wm * 64 + f * 16 + l16;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(sA + swz(r, lq));
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(sA + swz(r, lq + 4));
-                af[f] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-#pragma unroll
-            for (int x = 0; x < FN; ++x) {
-                const int r = wn * WN + x * 16 + l16;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(sB + swz(r, lq));
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(sB + swz(r, lq + 4));
-                const v8i bf = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int y = 0; y < FM; ++y)
-                    acc[x][y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf, af[y], acc[x][y], 0, 0, 0, sb_cur, 0, sa_cur[y]);
-            }
-            if (more) GFG_STORE_STAGE(buf ^ 1)
-            __syncthreads();
-            if (more) {
-#pragma unroll
-                for (int f = 0; f < FM; ++f) sa_cur[f] = sa_nxt[f];
-                sb_cur = sb_nxt;
-            }
+        // steady state: three steps per iteration (stage k in buffer k % 3),
+        // every step refills and reads, so the body has no branches
+        int kb = 0;
+        for (; kb + 5 < KB; kb += 3) {
+            k_step<BN, true, true, L>(c, buf0, buf1, kb + 3, wave, fa, fb, sa0, sb0, acc);
+            k_step<BN, true, true, L>(c, buf1, buf2, kb + 4, wave, fa, fb, sa1, sb1, acc);
+            k_step<BN, true, true, L>(c, buf2, buf0, kb + 5, wave, fa, fb, sa2, sb2, acc);
         }
-#undef GFG_LOAD_STAGE
-#undef GFG_LOAD_SCALES
-#undef GFG_STORE_STAGE
+        // tail: R = KB - kb steps remain (1..5); stage j+3 is refilled while j + 3 < KB
+        const int R = KB - kb;
+        if (R == 5) {
+            k_step<BN, true, true, L>(c, buf0, buf1, kb + 3, wave, fa, fb, sa0, sb0, acc);
+            k_step<BN, true, true, L>(c, buf1, buf2, kb + 4, wave, fa, fb, sa1, sb1, acc);
+            k_step<BN, false, true, L>(c, buf2, buf0, 0, wave, fa, fb, sa2, sb2, acc);
+            k_step<BN, false, true, 0>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
+            k_step<BN, false, false, 0>(c, buf1, buf2, 0, wave, fa, fb, sa1, sb1, acc);
+        } else if (R == 4) {
+            k_step<BN, true, true, L>(c, buf0, buf1, kb + 3, wave, fa, fb, sa0, sb0, acc);
+            k_step<BN, false, true, L>(c, buf1, buf2, 0, wave, fa, fb, sa1, sb1, acc);
+            k_step<BN, false, true, 0>(c, buf2, buf0, 0, wave, fa, fb, sa2, sb2, acc);
+            k_step<BN, false, false, 0>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
+        } else if (R == 3) {
+            k_step<BN, false, true, L>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
+            k_step<BN, false, true, 0>(c, buf1, buf2, 0, wave, fa, fb, sa1, sb1, acc);
+            k_step<BN, false, false, 0>(c, buf2, buf0, 0, wave, fa, fb, sa2, sb2, acc);
+        } else if (R == 2) {
+            k_step<BN, false, true, 0>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
+            k_step<BN, false, false, 0>(c, buf1, buf2, 0, wave, fa, fb, sa1, sb1, acc);
+        } else {
+            k_step<BN, false, false, 0>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
+        }
+        // every wave is done with LDS before the next tile's prologue refills it
+        GFG_WAITCNT(0, 0);
+        __builtin_amdgcn_s_barrier();
 
         // ---- epilogue: lane owns row (16y + l16), columns 16x + 4lq .. +3 -----
 #pragma unroll
@@ -344,8 +532,9 @@ int check_common(const char* fn, const void* a, const void* sa, const void* b, c
     if (N <= 0 || K <= 0) return fail(GFG_EINVAL, "%s: N=%lld K=%lld must be positive", fn, (long long)N, (long long)K);
     if (N % 128 || K % 128)
         return fail(GFG_EUNSUPPORTED, "%s: N=%lld and K=%lld must be multiples of 128", fn, (long long)N, (long long)K);
-    if (N > (int64_t(1) << 30) || K > (int64_t(1) << 30))
-        return fail(GFG_EUNSUPPORTED, "%s: N or K too large", fn);
+    if (N > (int64_t(1) << 30) || K > (int64_t(1) << 23))   // 32-bit in-tile offsets
+        return fail(GFG_EUNSUPPORTED, "%s: N=%lld or K=%lld too large (N <= 2^30, K <= 2^23)", fn,
+                    (long long)N, (long long)K);
     return GFG_OK;
 }
 

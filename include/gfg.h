@@ -73,8 +73,8 @@ enum gfg_out_dtype { GFG_OUT_BF16 = 0, GFG_OUT_F16 = 1 };
  * whose first row is padding is skipped).  A row whose entry differs from its
  * tile's expert is left untouched.
  *
- * Sizes: M >= 0 (M = 0 is a no-op), N > 0 and K > 0 multiples of 128
- * (else GFG_EUNSUPPORTED), 1 <= G <= 65535, ceil(M/128) <= 4096 (else
+ * Sizes: M >= 0 (M = 0 is a no-op), N > 0 and K > 0 multiples of 128 with
+ * N <= 2^30 and K <= 2^23 (else GFG_EUNSUPPORTED), 1 <= G <= 65535, ceil(M/128) <= 4096 (else
  * GFG_EUNSUPPORTED).
  */
 GFG_API int grouped_fp8_gemm_contiguous(const void* a, const uint8_t* a_scale,
@@ -93,7 +93,8 @@ GFG_API int grouped_fp8_gemm_contiguous(const void* a, const uint8_t* a_scale,
  *   masked_m  [G]                         int32, DEVICE memory: rows computed per group
  *   d         [G][M_max][N]               rows m < masked_m[g] written, others untouched
  *
- * Sizes: M_max >= 0, N and K positive multiples of 128, 1 <= G <= 65535,
+ * Sizes: M_max >= 0, N and K positive multiples of 128 (N <= 2^30, K <= 2^23),
+ * 1 <= G <= 65535,
  * G * ceil(M_max/128) <= 4096 (else GFG_EUNSUPPORTED).
  */
 GFG_API int grouped_fp8_gemm_masked(const void* a, const uint8_t* a_scale,
