@@ -37,7 +37,7 @@ namespace {
 
 constexpr int BM = 128;          // rows of A per tile (= scale block edge)
 constexpr int BK = 128;          // K per step (= one E8M0 block along K)
-constexpr int NTHREADS = 256;    // 4 wave64s, one per SIMD
+constexpr int NTHREADS = 512;    // 8 wave64s, two per SIMD
 constexpr int MT_MAX = 4096;     // largest number of candidate 128-row tiles
 constexpr int NUM_XCD = 8;
 
@@ -105,7 +105,7 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 template <int BN>
 struct TileCtx {
     static constexpr int WAVES = NTHREADS / 64;
-    static constexpr int WN = BN / 2;               // columns per wave (2 x 2 wave grid)
+    static constexpr int WN = BN / 4;               // columns per wave (2 x 4 wave grid)
     static constexpr int FN = WN / 16;              // 16-column MFMA tiles per wave
     static constexpr int FM = 4;                    // 16-row MFMA tiles per wave (64 rows)
     static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
@@ -132,7 +132,7 @@ struct TileCtx {
 template <int BN>
 struct Frags {
     v8i a[4];
-    v8i b[BN / 32];
+    v8i b[BN / 64];
 };
 
 // Issue stage kb's loads: its A/B tiles by LDS DMA into buffer `dst` (laid out
@@ -409,52 +409,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         Frags<BN> fa, fb;
         int sa0[4], sa1[4], sa2[4], sb0 = 0, sb1 = 0, sb2 = 0;
 
-        // prologue: stages 0..2 in flight, stage 0's fragments in `fa`
+        // prologue: stages 0..2 in flight (clamped to the last stage), stage 0's
+        // fragments in `fa`
         issue_stage<BN>(c, buf0, 0, wave, sa0, sb0);
-        if (KB >= 3) {
-            issue_stage<BN>(c, buf1, 1, wave, sa1, sb1);
-            issue_stage<BN>(c, buf2, 2, wave, sa2, sb2);
-            GFG_WAITCNT(2 * L, 15);
-        } else if (KB == 2) {
-            issue_stage<BN>(c, buf1, 1, wave, sa1, sb1);
-            GFG_WAITCNT(L, 15);
-        } else {
-            GFG_WAITCNT(0, 15);
-        }
+        issue_stage<BN>(c, buf1, min(1, KB - 1), wave, sa1, sb1);
+        issue_stage<BN>(c, buf2, min(2, KB - 1), wave, sa2, sb2);
+        GFG_WAITCNT(2 * L, 15);
         __builtin_amdgcn_s_barrier();
         read_frags<BN>(c, buf0, fa);
 
-        // steady state: three steps per iteration (stage k in buffer k % 3),
-        // every step refills and reads, so the body has no branches
+        // Every step has the same shape: it refills the buffer it frees with
+        // stage k+3 (past the end: the last stage again, into a buffer nobody
+        // reads any more) and reads stage k+1's fragments (past the end: unused).
         int kb = 0;
-        for (; kb + 5 < KB; kb += 3) {
-            k_step<BN, true, true, L>(c, buf0, buf1, kb + 3, wave, fa, fb, sa0, sb0, acc);
-            k_step<BN, true, true, L>(c, buf1, buf2, kb + 4, wave, fa, fb, sa1, sb1, acc);
-            k_step<BN, true, true, L>(c, buf2, buf0, kb + 5, wave, fa, fb, sa2, sb2, acc);
+        for (; kb + 3 <= KB; kb += 3) {
+            k_step<BN, true, true, L>(c, buf0, buf1, min(kb + 3, KB - 1), wave, fa, fb, sa0, sb0, acc);
+            k_step<BN, true, true, L>(c, buf1, buf2, min(kb + 4, KB - 1), wave, fa, fb, sa1, sb1, acc);
+            k_step<BN, true, true, L>(c, buf2, buf0, min(kb + 5, KB - 1), wave, fa, fb, sa2, sb2, acc);
         }
-        // tail: R = KB - kb steps remain (1..5); stage j+3 is refilled while j + 3 < KB
-        const int R = KB - kb;
-        if (R == 5) {
-            k_step<BN, true, true, L>(c, buf0, buf1, kb + 3, wave, fa, fb, sa0, sb0, acc);
-            k_step<BN, true, true, L>(c, buf1, buf2, kb + 4, wave, fa, fb, sa1, sb1, acc);
-            k_step<BN, false, true, L>(c, buf2, buf0, 0, wave, fa, fb, sa2, sb2, acc);
-            k_step<BN, false, true, 0>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
-            k_step<BN, false, false, 0>(c, buf1, buf2, 0, wave, fa, fb, sa1, sb1, acc);
-        } else if (R == 4) {
-            k_step<BN, true, true, L>(c, buf0, buf1, kb + 3, wave, fa, fb, sa0, sb0, acc);
-            k_step<BN, false, true, L>(c, buf1, buf2, 0, wave, fa, fb, sa1, sb1, acc);
-            k_step<BN, false, true, 0>(c, buf2, buf0, 0, wave, fa, fb, sa2, sb2, acc);
-            k_step<BN, false, false, 0>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
-        } else if (R == 3) {
-            k_step<BN, false, true, L>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
-            k_step<BN, false, true, 0>(c, buf1, buf2, 0, wave, fa, fb, sa1, sb1, acc);
-            k_step<BN, false, false, 0>(c, buf2, buf0, 0, wave, fa, fb, sa2, sb2, acc);
-        } else if (R == 2) {
-            k_step<BN, false, true, 0>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
-            k_step<BN, false, false, 0>(c, buf1, buf2, 0, wave, fa, fb, sa1, sb1, acc);
-        } else {
-            k_step<BN, false, false, 0>(c, buf0, buf1, 0, wave, fa, fb, sa0, sb0, acc);
-        }
+        if (KB - kb >= 1) k_step<BN, true, true, L>(c, buf0, buf1, KB - 1, wave, fa, fb, sa0, sb0, acc);
+        if (KB - kb >= 2) k_step<BN, true, true, L>(c, buf1, buf2, KB - 1, wave, fa, fb, sa1, sb1, acc);
         // every wave is done with LDS before the next tile's prologue refills it
         GFG_WAITCNT(0, 0);
         __builtin_amdgcn_s_barrier();

@@ -84,12 +84,22 @@ def standard_workloads() -> list[Workload]:
 
 
 def workload(name_or_index) -> Workload:
+    """A standard workload by index or name, or an ad-hoc one named
+    ``contig_g{G}_m{rows per group}_n{N}_k{K}`` or ``masked_g{G}_m{M_max}_n{N}_k{K}``
+    (every group full; bf16 out; seed 2000)."""
     ws = standard_workloads()
     if isinstance(name_or_index, int):
         return ws[name_or_index]
     for w in ws:
         if w.name == name_or_index:
             return w
+    import re
+    m = re.fullmatch(r"(contig|masked)_g(\d+)_m(\d+)_n(\d+)_k(\d+)", name_or_index)
+    if m:
+        kind, G, rows, N, K = m.group(1), *(int(v) for v in m.groups()[1:])
+        if kind == "contig":
+            return Workload(name_or_index, "contiguous", G, N, K, "bf16", 2000, m_per_group=[rows] * G)
+        return Workload(name_or_index, "masked", G, N, K, "bf16", 2000, M_max=rows, masked_m=[rows] * G)
     raise KeyError(name_or_index)
 
 
