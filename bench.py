@@ -34,8 +34,13 @@ KERNEL_SRC = os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", "gfg_gemm.hip")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: // comments and blank lines removed,
+    so an edit to comments alone keeps stored counter results valid."""
+    import re
+    with open(KERNEL_SRC) as f:
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def algorithmic_bytes(w, layout=None) -> int:
@@ -66,6 +71,54 @@ def traffic_from_profile(w):
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def _pmc_per_dispatch(root, counter):
+    """{kernel name: average per dispatch} of one counter from a rocprofv3 --pmc csv run."""
+    import collections
+    import csv
+    import glob
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    files = glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {root}")
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: (sum(d.values()) / len(d), len(d)) for k, d in per.items()}
+
+
+def summarize_traffic(workload, fetch_dir, write_dir, copy_bytes):
+    """HBM bytes per launch of the GEMM kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) divided by what the same counter reads per byte for the plain copy
+    kernel of known size that the run also launched."""
+    from fp8_block_scaled_amd import workloads as wl
+    w = wl.workload(workload)
+    out = {"workload": w.name, "kernel_source_sha256_16": kernel_source_hash()}
+    total = 0.0
+    for counter, root in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _pmc_per_dispatch(root, counter)
+        gemm = [v for k, v in per.items() if "grouped_fp8_gemm" in k]
+        copy = [(k, v) for k, v in per.items() if "neg" in k.lower()]
+        if not gemm or not copy:
+            raise SystemExit(f"{counter}: need both the GEMM and the copy kernel in {root}: {list(per)}")
+        ck, (cval, _) = copy[0]
+        factor = cval * 1024.0 / copy_bytes
+        gbytes = gemm[0][0] * 1024.0 / factor
+        total += gbytes
+        out[counter] = {"gemm_KiB_per_dispatch": round(gemm[0][0], 1), "gemm_dispatches": gemm[0][1],
+                        "copy_kernel": ck, "copy_bytes": copy_bytes, "copy_KiB_per_dispatch": round(cval, 1),
+                        "factor": round(factor, 4), "gemm_bytes_per_launch": int(gbytes)}
+    out["hbm_bytes_per_launch"] = int(total)
+    out["algorithmic_bytes_per_launch"] = algorithmic_bytes(w)
+    out["traffic_over_algorithmic"] = round(total / algorithmic_bytes(w), 3)
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(w, x):
@@ -100,7 +153,18 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 256 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run a plain copy kernel (torch.neg) over this many bytes 5 times "
+                         "(the calibration kernel of the FETCH_SIZE / WRITE_SIZE counter passes)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                         "'bench.py --copy-bytes B' into profiles/traffic_<workload>.json, then exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        if not args.copy_bytes:
+            raise SystemExit("--traffic-from needs the --copy-bytes the counter runs used")
+        summarize_traffic(args.workload, *args.traffic_from, args.copy_bytes)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the grouped GEMM has no "
                                    "multi-GPU path here (experts would be sharded across GPUs with "
@@ -204,6 +268,16 @@ def main():
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, x0)
     print(json.dumps(res), flush=True)
+    if args.copy_bytes:
+        del sets, calls
+        # one elementwise kernel per call that reads and writes copy_bytes each
+        # (a driver memcpy may be split over several dispatches)
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize(dev)
 
 
 if __name__ == "__main__":

@@ -9,17 +9,21 @@
 // hardware-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4.
 //
 // Design (gfx950-first):
-//  * one persistent workgroup of 4 wave64s per CU slot; the grid walks a
-//    device-built list of valid (expert, 128-row) tiles, so padding tiles
-//    (contiguous) and masked-off tiles (masked) cost nothing;
+//  * one persistent workgroup of 8 wave64s (two per SIMD) per CU; the grid
+//    walks a device-built list of valid (expert, 128-row) tiles, so padding
+//    tiles (contiguous) and masked-off tiles (masked) cost nothing;
 //  * tile order: grouped-M traversal inside contiguous per-XCD ranges (the
 //    hardware deals workgroups round-robin over the 8 XCDs, so workgroup w
 //    sits on XCD w % 8 and each XCD's L2 sees neighbouring tiles);
 //  * a 128 x BN x 128 block tile per K-step: exactly one scale block along
 //    K, so each MFMA takes its A and B scale bytes straight from the
 //    E8M0 tensors;
-//  * A/B tiles double-buffered in LDS with a 16-byte-chunk XOR swizzle;
-//    global loads for step k+1 are in flight while step k computes;
+//  * three LDS stages per tile, filled by direct-to-LDS global loads
+//    (global_load_lds, 16 B per lane) through a 16-byte-chunk XOR swizzle;
+//    the loads for step k+3 are issued while step k computes, with explicit
+//    vmcnt waits counted per step;
+//  * waves laid out 2 (M) x 4 (N), 64 x BN/4 outputs each; fragments for
+//    step k+1 are read from LDS while the MFMAs of step k run;
 //  * the MFMA's first operand is the B tile (N rows) and its second the A
 //    tile (M rows), so each lane ends up owning 4 consecutive output columns
 //    of one row, written as one 8-byte store.

@@ -400,4 +400,44 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     except AssertionError:
         failures += 1
     monkeypatch.setattr(o, "grouped_gemm_contiguous", real_gc)
-    assert failures == 3
+    # truncating encoder: round toward zero instead of to nearest even
+    real_enc = o.encode_e4m3_rne
+
+    def trunc_enc(x):
+        c = real_enc(x)
+        over = np.abs(o.decode_e4m3(c)) > np.abs(np.asarray(x, np.float64))
+        return np.where(over, c - 1, c).astype(np.uint8)
+    monkeypatch.setattr(o, "encode_e4m3_rne", trunc_enc)
+    try:
+        test_encode_bruteforce_sample()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "encode_e4m3_rne", real_enc)
+    # activation scale dropped in the dequantization
+    real_da = o.dequantize_act
+    monkeypatch.setattr(o, "dequantize_act", lambda q, s: o.decode_e4m3(q))
+    try:
+        test_contiguous_gemm_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "dequantize_act", real_da)
+    # E8M0 bias off by one (2^(b-128))
+    real_ev = o.e8m0_value
+    monkeypatch.setattr(o, "e8m0_value", lambda b: real_ev(b) / 2)
+    try:
+        test_masked_gemm_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "e8m0_value", real_ev)
+    # masked op computing every row of the group buffer, not only m < masked_m
+    real_gm = o.grouped_gemm_masked
+
+    def wrong_gm(qa, sa, qb, sb, masked_m, d_init=None):
+        return real_gm(qa, sa, qb, sb, np.full_like(np.asarray(masked_m), qa.shape[1]), d_init)
+    monkeypatch.setattr(o, "grouped_gemm_masked", wrong_gm)
+    try:
+        test_masked_gemm_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "grouped_gemm_masked", real_gm)
+    assert failures == 7
