@@ -105,6 +105,19 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
     return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
 }
 
+// The 4-byte word holding scale byte kb of a row, read as one global dword
+// (the byte is extracted where it is used, so no zero-extension of a freshly
+// loaded register forces a wait).  An aligned word that contains a byte of an
+// allocation lies in the same page as that byte, so the read never touches
+// unmapped memory.
+typedef const __attribute__((address_space(1))) uint32_t gword_t;
+__device__ __forceinline__ int load_scale_word(const uint8_t* row, int kb) {
+    return int(*reinterpret_cast<gword_t*>(reinterpret_cast<uintptr_t>(row + kb) & ~uintptr_t(3)));
+}
+__device__ __forceinline__ int scale_byte(int word, const uint8_t* row, int kb) {
+    return (word >> (8 * int((reinterpret_cast<uintptr_t>(row) + uintptr_t(kb)) & 3))) & 0xff;
+}
+
 // Per-tile, per-lane constants of the K loop.
 template <int BN>
 struct TileCtx {
@@ -123,7 +136,7 @@ struct TileCtx {
     const uint8_t* a_tile;            // A row m0, K 0 of the region
     const uint8_t* b_tile;            // B row n0 of expert g, K 0
     __amdgpu_buffer_rsrc_t sa_rsrc;   // scale_a from row m0 of K-block 0 to the region's end
-    __amdgpu_buffer_rsrc_t sb_rsrc;   // scale_b row of this wave's 128-column block
+    const uint8_t* sb_row;            // scale_b row (all K-blocks) of this wave's 128-column block
     uint32_t sa_stride;        // scale_a bytes between K-blocks (rows of the region)
     uint32_t a_off[A_DMA];     // per-lane source offsets of this wave's DMA chunks
     uint32_t b_off[B_DMA];
@@ -148,7 +161,7 @@ __device__ __forceinline__ void issue_stage(const TileCtx<BN>& c, GFG_LDS uint8_
     const uint32_t so = uint32_t(kb) * c.sa_stride;
 #pragma unroll
     for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(c.sa_rsrc, c.sa_off[f], so, 0);
-    sb = __builtin_amdgcn_raw_buffer_load_b8(c.sb_rsrc, 0, kb, 0);
+    sb = load_scale_word(c.sb_row, kb);
     // K-block base pointers made opaque scalars, so each DMA address is a scalar
     // base plus this lane's 32-bit offset (no per-lane 64-bit induction variables)
     const uint8_t* ak = uniform_ptr(c.a_tile + int64_t(kb) * BK);
@@ -218,17 +231,20 @@ __device__ __forceinline__ void sched_pattern() {
 
 template <int BN, bool ISSUE, bool READ, int VMWAIT>
 __device__ __forceinline__ void k_step(const TileCtx<BN>& c, GFG_LDS uint8_t* __restrict__ refill,
-                                       const GFG_LDS uint8_t* __restrict__ next, int kb_refill, int wave,
+                                       const GFG_LDS uint8_t* __restrict__ next, int kb_cur, int kb_refill,
+                                       int wave,
                                        Frags<BN>& cur, Frags<BN>& nxt, int (&sa)[4], int& sb,
                                        v4f (&acc)[TileCtx<BN>::FN][4]) {
     using C = TileCtx<BN>;
     __builtin_amdgcn_sched_barrier(0);
     GFG_WAITCNT(VMWAIT, 0);
     __builtin_amdgcn_s_barrier();
+    // nothing that reads this step's scale registers may rise above the wait
+    __builtin_amdgcn_sched_barrier(0);
     int sa_use[4];
 #pragma unroll
     for (int y = 0; y < 4; ++y) sa_use[y] = sa[y];
-    const int sb_use = sb;
+    const int sb_use = scale_byte(sb, c.sb_row, kb_cur);
     // The LDS DMA and the fragment reads are issued here, through this
     // function's restrict parameters, so the compiler knows the refilled
     // buffer and the buffer being read do not overlap and adds no wait for
@@ -265,7 +281,7 @@ __device__ __forceinline__ void k_step(const TileCtx<BN>& c, GFG_LDS uint8_t* __
         const uint32_t so = uint32_t(kb_refill) * c.sa_stride;
 #pragma unroll
         for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(c.sa_rsrc, c.sa_off[f], so, 0);
-        sb = __builtin_amdgcn_raw_buffer_load_b8(c.sb_rsrc, 0, kb_refill, 0);
+        sb = load_scale_word(c.sb_row, kb_refill);
     }
     sched_pattern<0, C::FN * C::FM, ISSUE ? C::A_DMA + C::B_DMA : 0, READ ? 2 * (C::FM + C::FN) : 0,
                   ISSUE ? C::FM + 1 : 0>();
@@ -374,7 +390,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         c.a_tile = a_reg + m0 * p.K;
         c.b_tile = p.b + (int64_t(g) * p.N + n0) * p.K;
         c.sa_rsrc = make_rsrc(sa_reg + m0, uint32_t(int64_t(KB) * p.rows - m0));
-        c.sb_rsrc = make_rsrc(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB, uint32_t(KB));
+        c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB);
         c.sa_stride = uint32_t(p.rows);
         // DMA chunk j of this wave fills LDS rows 8*(j*WAVES + wave) .. +7; lane i
         // writes physical chunk i%8 of row +i/8, which holds logical chunk
@@ -427,12 +443,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         // reads any more) and reads stage k+1's fragments (past the end: unused).
         int kb = 0;
         for (; kb + 3 <= KB; kb += 3) {
-            k_step<BN, true, true, L>(c, buf0, buf1, min(kb + 3, KB - 1), wave, fa, fb, sa0, sb0, acc);
-            k_step<BN, true, true, L>(c, buf1, buf2, min(kb + 4, KB - 1), wave, fa, fb, sa1, sb1, acc);
-            k_step<BN, true, true, L>(c, buf2, buf0, min(kb + 5, KB - 1), wave, fa, fb, sa2, sb2, acc);
+            k_step<BN, true, true, L>(c, buf0, buf1, kb, min(kb + 3, KB - 1), wave, fa, fb, sa0, sb0, acc);
+            k_step<BN, true, true, L>(c, buf1, buf2, kb + 1, min(kb + 4, KB - 1), wave, fa, fb, sa1, sb1, acc);
+            k_step<BN, true, true, L>(c, buf2, buf0, kb + 2, min(kb + 5, KB - 1), wave, fa, fb, sa2, sb2, acc);
         }
-        if (KB - kb >= 1) k_step<BN, true, true, L>(c, buf0, buf1, KB - 1, wave, fa, fb, sa0, sb0, acc);
-        if (KB - kb >= 2) k_step<BN, true, true, L>(c, buf1, buf2, KB - 1, wave, fa, fb, sa1, sb1, acc);
+        if (KB - kb >= 1) k_step<BN, true, true, L>(c, buf0, buf1, kb, KB - 1, wave, fa, fb, sa0, sb0, acc);
+        if (KB - kb >= 2) k_step<BN, true, true, L>(c, buf1, buf2, kb + 1, KB - 1, wave, fa, fb, sa1, sb1, acc);
         // every wave is done with LDS before the next tile's prologue refills it
         GFG_WAITCNT(0, 0);
         __builtin_amdgcn_s_barrier();
