@@ -148,8 +148,10 @@ def cpu_baseline(w, x):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    # The GPU's clock needs a few hundred ms of sustained load to settle at its
+    # loaded frequency; a short warmup times part of the ramp.
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 256 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")

@@ -70,6 +70,11 @@ struct Params {
 // per row covering its 8 chunks).
 __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
 
+// The A tile's swizzle keys on (r >> 2) & 7 instead: an A fragment takes rows
+// 4 apart (row 4*l16 + f of the wave's 64, so that a lane's four rows have
+// adjacent scale bytes), and this key keeps those reads conflict-free.
+__device__ __forceinline__ int swz_a(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 7)) << 4); }
+
 template <bool MASKED>
 __device__ __forceinline__ bool cand_valid(const Params& p, int c, int* g_out) {
     if (MASKED) {
@@ -118,9 +123,13 @@ __device__ __forceinline__ int scale_byte(int word, const uint8_t* row, int kb) 
     return (word >> (8 * int((reinterpret_cast<uintptr_t>(row) + uintptr_t(kb)) & 3))) & 0xff;
 }
 
-// Per-tile, per-lane constants of the K loop.
-template <int BN>
+// Per-tile, per-lane constants of the K loop.  SAW: the lane's four A-scale
+// bytes (rows 4*l16 .. 4*l16+3 of its wave's 64) are read as one aligned dword
+// (scale rows a multiple of 4 bytes apart); otherwise as four bytes.
+template <int BN_, bool SAW_>
 struct TileCtx {
+    static constexpr int BN = BN_;
+    static constexpr bool SAW = SAW_;
     static constexpr int WAVES = NTHREADS / 64;
     static constexpr int WN = BN / 4;               // columns per wave (2 x 4 wave grid)
     static constexpr int FN = WN / 16;              // 16-column MFMA tiles per wave
@@ -128,8 +137,10 @@ struct TileCtx {
     static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
     static constexpr int A_DMA = A_BYTES / 1024 / WAVES;   // 1 KB LDS-DMA wave instructions per stage
     static constexpr int B_DMA = B_BYTES / 1024 / WAVES;
-    // vector-memory loads one wave issues per stage: DMAs plus FM + 1 scale bytes
-    static constexpr int LOADS = A_DMA + B_DMA + FM + 1;
+    // vector-memory loads one wave issues per stage: DMAs, the A scales (one
+    // dword or FM bytes) and the B-scale dword
+    static constexpr int SA_LOADS = SAW ? 1 : FM;
+    static constexpr int LOADS = A_DMA + B_DMA + SA_LOADS + 1;
 
     // Buffer resources (scalar registers): base + byte count.  The hardware
     // returns zero for any offset past the count instead of touching memory.
@@ -140,7 +151,7 @@ struct TileCtx {
     uint32_t sa_stride;        // scale_a bytes between K-blocks (rows of the region)
     uint32_t a_off[A_DMA];     // per-lane source offsets of this wave's DMA chunks
     uint32_t b_off[B_DMA];
-    uint32_t sa_off[TileCtx::FM];
+    uint32_t sa_off[4];        // A-scale byte offsets (SAW: [0] only, the dword)
     // LDS byte offsets of this lane's fragment row, logical chunks lq (lo) and
     // lq + 4 (hi); with the XOR swizzle the hi chunk sits at lo ^ 64.
     int a_lo, a_hi, b_lo, b_hi;
@@ -152,15 +163,31 @@ struct Frags {
     v8i b[BN / 64];
 };
 
-// Issue stage kb's loads: its A/B tiles by LDS DMA into buffer `dst` (laid out
-// with swz()) and this lane's scale bytes into (sa, sb).
-template <int BN>
-__device__ __forceinline__ void issue_stage(const TileCtx<BN>& c, GFG_LDS uint8_t* __restrict__ dst,
-                                            int kb, int wave, int (&sa)[4], int& sb) {
-    using C = TileCtx<BN>;
+// This lane's A-scale loads for stage kb (one dword, or FM bytes).
+template <class C>
+__device__ __forceinline__ void load_sa(const C& c, int kb, int (&sa)[4]) {
     const uint32_t so = uint32_t(kb) * c.sa_stride;
+    if constexpr (C::SAW) {
+        sa[0] = int(__builtin_amdgcn_raw_buffer_load_b32(c.sa_rsrc, c.sa_off[0], so, 0));
+    } else {
 #pragma unroll
-    for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(c.sa_rsrc, c.sa_off[f], so, 0);
+        for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(c.sa_rsrc, c.sa_off[f], so, 0);
+    }
+}
+
+// The packed A-scale word of a stage: byte f = scale of fragment f's row.
+template <class C>
+__device__ __forceinline__ int sa_word(const int (&sa)[4]) {
+    if constexpr (C::SAW) return sa[0];
+    else return (sa[0] & 0xff) | ((sa[1] & 0xff) << 8) | ((sa[2] & 0xff) << 16) | (sa[3] << 24);
+}
+
+// Issue stage kb's loads: its A/B tiles by LDS DMA into buffer `dst` (A laid
+// out with swz_a(), B with swz()) and this lane's scales into (sa, sb).
+template <class C>
+__device__ __forceinline__ void issue_stage(const C& c, GFG_LDS uint8_t* __restrict__ dst,
+                                            int kb, int wave, int (&sa)[4], int& sb) {
+    load_sa(c, kb, sa);
     sb = load_scale_word(c.sb_row, kb);
     // K-block base pointers made opaque scalars, so each DMA address is a scalar
     // base plus this lane's 32-bit offset (no per-lane 64-bit induction variables)
@@ -177,15 +204,15 @@ __device__ __forceinline__ void issue_stage(const TileCtx<BN>& c, GFG_LDS uint8_
 }
 
 // Read this lane's fragments of one stage from LDS.  A fragment (16 rows x 128 K):
-// lane (l16, lq) holds row l16's 16-byte chunks lq and lq + 4.
-template <int BN>
-__device__ __forceinline__ void read_frags(const TileCtx<BN>& c, const GFG_LDS uint8_t* __restrict__ src,
-                                           Frags<BN>& f) {
-    using C = TileCtx<BN>;
+// lane (l16, lq) holds one row's 16-byte chunks lq and lq + 4; A fragment y
+// takes row 4*l16 + y of the wave's 64 rows, B fragment x row 16x + l16 of its WN.
+template <class C>
+__device__ __forceinline__ void read_frags(const C& c, const GFG_LDS uint8_t* __restrict__ src,
+                                           Frags<C::BN>& f) {
 #pragma unroll
     for (int y = 0; y < C::FM; ++y) {
-        const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + c.a_lo + y * 16 * BK);
-        const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + c.a_hi + y * 16 * BK);
+        const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + c.a_lo + y * BK);
+        const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + c.a_hi + y * BK);
         f.a[y] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
@@ -196,15 +223,23 @@ __device__ __forceinline__ void read_frags(const TileCtx<BN>& c, const GFG_LDS u
     }
 }
 
-template <int BN>
-__device__ __forceinline__ void mfma_stage(const Frags<BN>& f, const int (&sa)[4], int sb,
-                                           v4f (&acc)[TileCtx<BN>::FN][4]) {
+// MFMAs of A fragment Y against every B fragment: the A scale is byte Y of
+// the packed word (op_sel picks it), the B scale the wave's byte.
+template <class C, int Y>
+__device__ __forceinline__ void mfma_row(const Frags<C::BN>& f, int saw, int sb, v4f (&acc)[C::FN][4]) {
 #pragma unroll
-    for (int x = 0; x < TileCtx<BN>::FN; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-            acc[x][y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[x], f.a[y], acc[x][y], 0, 0, 0,
-                                                                         sb, 0, sa[y]);
+    for (int x = 0; x < C::FN; ++x)
+        acc[x][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[x], f.a[Y], acc[x][Y], 0, 0, 0, sb, Y,
+                                                                     saw);
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_stage(const Frags<C::BN>& f, int saw, int sb, v4f (&acc)[C::FN][4]) {
+    static_assert(C::FM == 4, "four A fragments per wave");
+    mfma_row<C, 0>(f, saw, sb, acc);
+    mfma_row<C, 1>(f, saw, sb, acc);
+    mfma_row<C, 2>(f, saw, sb, acc);
+    mfma_row<C, 3>(f, saw, sb, acc);
 }
 
 // One K-step k.  On entry: fragments of stage k are in `cur` (their LDS reads
@@ -229,21 +264,18 @@ __device__ __forceinline__ void sched_pattern() {
     }
 }
 
-template <int BN, bool ISSUE, bool READ, int VMWAIT>
-__device__ __forceinline__ void k_step(const TileCtx<BN>& c, GFG_LDS uint8_t* __restrict__ refill,
+template <class C, bool ISSUE, bool READ, int VMWAIT>
+__device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__ refill,
                                        const GFG_LDS uint8_t* __restrict__ next, int kb_cur, int kb_refill,
                                        int wave,
-                                       Frags<BN>& cur, Frags<BN>& nxt, int (&sa)[4], int& sb,
-                                       v4f (&acc)[TileCtx<BN>::FN][4]) {
-    using C = TileCtx<BN>;
+                                       Frags<C::BN>& cur, Frags<C::BN>& nxt, int (&sa)[4], int& sb,
+                                       v4f (&acc)[C::FN][4]) {
     __builtin_amdgcn_sched_barrier(0);
     GFG_WAITCNT(VMWAIT, 0);
     __builtin_amdgcn_s_barrier();
     // nothing that reads this step's scale registers may rise above the wait
     __builtin_amdgcn_sched_barrier(0);
-    int sa_use[4];
-#pragma unroll
-    for (int y = 0; y < 4; ++y) sa_use[y] = sa[y];
+    const int sa_use = sa_word<C>(sa);
     const int sb_use = scale_byte(sb, c.sb_row, kb_cur);
     // The LDS DMA and the fragment reads are issued here, through this
     // function's restrict parameters, so the compiler knows the refilled
@@ -265,8 +297,8 @@ __device__ __forceinline__ void k_step(const TileCtx<BN>& c, GFG_LDS uint8_t* __
     if (READ) {
 #pragma unroll
         for (int y = 0; y < C::FM; ++y) {
-            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + c.a_lo + y * 16 * BK);
-            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + c.a_hi + y * 16 * BK);
+            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + c.a_lo + y * BK);
+            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + c.a_hi + y * BK);
             nxt.a[y] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
@@ -276,22 +308,20 @@ __device__ __forceinline__ void k_step(const TileCtx<BN>& c, GFG_LDS uint8_t* __
             nxt.b[x] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     }
-    mfma_stage<BN>(cur, sa_use, sb_use, acc);
+    mfma_stage<C>(cur, sa_use, sb_use, acc);
     if (ISSUE) {   // after the MFMAs that read the old scale registers
-        const uint32_t so = uint32_t(kb_refill) * c.sa_stride;
-#pragma unroll
-        for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(c.sa_rsrc, c.sa_off[f], so, 0);
+        load_sa(c, kb_refill, sa);
         sb = load_scale_word(c.sb_row, kb_refill);
     }
     sched_pattern<0, C::FN * C::FM, ISSUE ? C::A_DMA + C::B_DMA : 0, READ ? 2 * (C::FM + C::FN) : 0,
-                  ISSUE ? C::FM + 1 : 0>();
+                  ISSUE ? C::SA_LOADS + 1 : 0>();
     if (READ) cur = nxt;
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BN, bool MASKED, typename OutT>
+template <int BN, bool MASKED, bool SAW, typename OutT>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p) {
-    using C = TileCtx<BN>;
+    using C = TileCtx<BN, SAW>;
     constexpr int FN = C::FN, FM = C::FM, WN = C::WN;
     constexpr int L = C::LOADS;
 
@@ -386,37 +416,48 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         }
         const int n0 = nt * BN;
 
-        TileCtx<BN> c;
+        C c;
         c.a_tile = a_reg + m0 * p.K;
         c.b_tile = p.b + (int64_t(g) * p.N + n0) * p.K;
         c.sa_rsrc = make_rsrc(sa_reg + m0, uint32_t(int64_t(KB) * p.rows - m0));
         c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB);
         c.sa_stride = uint32_t(p.rows);
         // DMA chunk j of this wave fills LDS rows 8*(j*WAVES + wave) .. +7; lane i
-        // writes physical chunk i%8 of row +i/8, which holds logical chunk
-        // (i%8) ^ (row & 7) of that row.
+        // writes physical chunk i%8 of tile row R = +i/8, which holds logical
+        // chunk (i%8) ^ key(R) of that row (A: key (R >> 2) & 7, B: R & 7).
         {
-            const int rr = lane >> 3, pc = lane & 7, lc = pc ^ rr;   // (row & 7) == rr
+            const int rr = lane >> 3, pc = lane & 7;
 #pragma unroll
             for (int j = 0; j < C::A_DMA; ++j) {
-                int64_t row = m0 + 8 * (j * C::WAVES + wave) + rr;
+                const int r = 8 * (j * C::WAVES + wave) + rr;
+                const int lc = pc ^ ((r >> 2) & 7);
+                int64_t row = m0 + r;
                 row = row < mlimit ? row : mlimit - 1;           // clamp: never read outside
                 c.a_off[j] = uint32_t(row - m0) * uint32_t(p.K) + uint32_t(lc * 16);
             }
 #pragma unroll
             for (int j = 0; j < C::B_DMA; ++j)
-                c.b_off[j] = uint32_t(8 * (j * C::WAVES + wave) + rr) * uint32_t(p.K) + uint32_t(lc * 16);
+                c.b_off[j] = uint32_t(8 * (j * C::WAVES + wave) + rr) * uint32_t(p.K) + uint32_t((pc ^ rr) * 16);
         }
+        // A-scale offsets (from row m0 of K-block 0): the lane's rows are
+        // wm*64 + 4*l16 + f.  The dword form needs no clamp: rows come in
+        // aligned fours that are all valid or all past the region's end, where
+        // the buffer read returns 0 (such rows are never stored).
+        if constexpr (SAW) {
+            c.sa_off[0] = uint32_t(wm * 64 + 4 * l16);
+        } else {
 #pragma unroll
-        for (int f = 0; f < FM; ++f) {
-            int64_t row = m0 + wm * 64 + f * 16 + l16;
-            row = row < mlimit ? row : mlimit - 1;
-            c.sa_off[f] = uint32_t(row - m0);
+            for (int f = 0; f < FM; ++f) {
+                int64_t row = m0 + wm * 64 + 4 * l16 + f;
+                row = row < mlimit ? row : mlimit - 1;
+                c.sa_off[f] = uint32_t(row - m0);
+            }
         }
-        // fragment rows: A row wm*64 + y*16 + l16, B row wn*WN + x*16 + l16; the
-        // swizzle term (row & 7) == (l16 & 7) for all y, x.
-        c.a_lo = swz(wm * 64 + l16, lq);
-        c.a_hi = swz(wm * 64 + l16, lq + 4);
+        // fragment rows: A row wm*64 + 4*l16 + y (swizzle key l16 & 7 for every
+        // y, so fragment y sits y rows below fragment 0), B row wn*WN + x*16 + l16
+        // (key l16 & 7).
+        c.a_lo = swz_a(wm * 64 + 4 * l16, lq);
+        c.a_hi = swz_a(wm * 64 + 4 * l16, lq + 4);
         c.b_lo = swz(wn * WN + l16, lq);
         c.b_hi = swz(wn * WN + l16, lq + 4);
 
@@ -431,32 +472,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
 
         // prologue: stages 0..2 in flight (clamped to the last stage), stage 0's
         // fragments in `fa`
-        issue_stage<BN>(c, buf0, 0, wave, sa0, sb0);
-        issue_stage<BN>(c, buf1, min(1, KB - 1), wave, sa1, sb1);
-        issue_stage<BN>(c, buf2, min(2, KB - 1), wave, sa2, sb2);
+        issue_stage(c, buf0, 0, wave, sa0, sb0);
+        issue_stage(c, buf1, min(1, KB - 1), wave, sa1, sb1);
+        issue_stage(c, buf2, min(2, KB - 1), wave, sa2, sb2);
         GFG_WAITCNT(2 * L, 15);
         __builtin_amdgcn_s_barrier();
-        read_frags<BN>(c, buf0, fa);
+        read_frags(c, buf0, fa);
 
         // Every step has the same shape: it refills the buffer it frees with
         // stage k+3 (past the end: the last stage again, into a buffer nobody
         // reads any more) and reads stage k+1's fragments (past the end: unused).
         int kb = 0;
         for (; kb + 3 <= KB; kb += 3) {
-            k_step<BN, true, true, L>(c, buf0, buf1, kb, min(kb + 3, KB - 1), wave, fa, fb, sa0, sb0, acc);
-            k_step<BN, true, true, L>(c, buf1, buf2, kb + 1, min(kb + 4, KB - 1), wave, fa, fb, sa1, sb1, acc);
-            k_step<BN, true, true, L>(c, buf2, buf0, kb + 2, min(kb + 5, KB - 1), wave, fa, fb, sa2, sb2, acc);
+            k_step<C, true, true, L>(c, buf0, buf1, kb, min(kb + 3, KB - 1), wave, fa, fb, sa0, sb0, acc);
+            k_step<C, true, true, L>(c, buf1, buf2, kb + 1, min(kb + 4, KB - 1), wave, fa, fb, sa1, sb1, acc);
+            k_step<C, true, true, L>(c, buf2, buf0, kb + 2, min(kb + 5, KB - 1), wave, fa, fb, sa2, sb2, acc);
         }
-        if (KB - kb >= 1) k_step<BN, true, true, L>(c, buf0, buf1, kb, KB - 1, wave, fa, fb, sa0, sb0, acc);
-        if (KB - kb >= 2) k_step<BN, true, true, L>(c, buf1, buf2, kb + 1, KB - 1, wave, fa, fb, sa1, sb1, acc);
+        if (KB - kb >= 1) k_step<C, true, true, L>(c, buf0, buf1, kb, KB - 1, wave, fa, fb, sa0, sb0, acc);
+        if (KB - kb >= 2) k_step<C, true, true, L>(c, buf1, buf2, kb + 1, KB - 1, wave, fa, fb, sa1, sb1, acc);
         // every wave is done with LDS before the next tile's prologue refills it
         GFG_WAITCNT(0, 0);
         __builtin_amdgcn_s_barrier();
 
-        // ---- epilogue: lane owns row (16y + l16), columns 16x + 4lq .. +3 -----
+        // ---- epilogue: lane owns row (4*l16 + y), columns 16x + 4lq .. +3 ----
 #pragma unroll
         for (int y = 0; y < FM; ++y) {
-            const int64_t row = m0 + wm * 64 + y * 16 + l16;
+            const int64_t row = m0 + wm * 64 + 4 * l16 + y;
             bool ok = row < mlimit;
             if (!MASKED && ok) ok = p.meta[row] == g;
             if (!ok) continue;
@@ -494,7 +535,7 @@ int device_info(DeviceInfo* out) {
     return GFG_OK;
 }
 
-template <int BN, bool MASKED, typename OutT>
+template <int BN, bool MASKED, bool SAW, typename OutT>
 int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     DeviceInfo di;
     if (int rc = device_info(&di)) return rc;
@@ -503,18 +544,31 @@ int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     unsigned grid = upper < unsigned(di.cus) ? upper : unsigned(di.cus);
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;          // whole slots on every XCD
     if (grid == 0) return GFG_OK;
-    hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, OutT>), dim3(grid), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, SAW, OutT>), dim3(grid), dim3(NTHREADS), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(GFG_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GFG_OK;
 }
 
+template <bool MASKED, bool SAW>
+int dispatch_w(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
+    const bool bf16 = out_dtype == GFG_OUT_BF16;
+    if constexpr (SAW) {
+        if (p.N % 256 == 0)
+            return bf16 ? launch_t<256, MASKED, true, __bf16>(p, n_cand, s)
+                        : launch_t<256, MASKED, true, _Float16>(p, n_cand, s);
+    }
+    // the byte-wise A-scale fallback keeps more registers live per stage and
+    // stays on the 128-column tile, which has room for them
+    return bf16 ? launch_t<128, MASKED, SAW, __bf16>(p, n_cand, s) : launch_t<128, MASKED, SAW, _Float16>(p, n_cand, s);
+}
+
+// The packed A-scale path needs every scale row (and so every aligned group of
+// four rows) to start on a 4-byte boundary.
 template <bool MASKED>
 int dispatch(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
-    const bool wide = p.N % 256 == 0;
-    if (out_dtype == GFG_OUT_BF16)
-        return wide ? launch_t<256, MASKED, __bf16>(p, n_cand, s) : launch_t<128, MASKED, __bf16>(p, n_cand, s);
-    return wide ? launch_t<256, MASKED, _Float16>(p, n_cand, s) : launch_t<128, MASKED, _Float16>(p, n_cand, s);
+    const bool saw = p.rows % 4 == 0 && reinterpret_cast<uintptr_t>(p.a_scale) % 4 == 0;
+    return saw ? dispatch_w<MASKED, true>(p, n_cand, out_dtype, s) : dispatch_w<MASKED, false>(p, n_cand, out_dtype, s);
 }
 
 int check_common(const char* fn, const void* a, const void* sa, const void* b, const void* sb,

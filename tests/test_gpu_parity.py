@@ -71,6 +71,22 @@ def test_overpadded_contiguous_layout():
     _check_contig(d, ref, layout, "bf16", "overpadded")
 
 
+@pytest.mark.parametrize("M,N", [(158, 512), (157, 384)])
+def test_contiguous_unpadded_tail(M, N):
+    """The last expert's run is cut short of a 128 multiple, so M is not a
+    multiple of 4 and the A-scale rows are not dword aligned (byte-wise scale
+    path); rows past M do not exist."""
+    rng = np.random.default_rng(23 + M)
+    layout = np.concatenate([np.full(100, 0), np.full(28, -1), np.full(M - 128, 1)]).astype(np.int32)
+    K = 384
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[layout < 0] = 0.0
+    b = rng.standard_normal((2, N, K)).astype(np.float32)
+    x = dict(a=a, b=b, grouped_layout=layout)
+    d, ref = _contig_case(x, "bf16")
+    _check_contig(d, ref, layout, "bf16", f"unpadded tail M={M} N={N}")
+
+
 def test_out_of_range_expert_ids_are_padding():
     rng = np.random.default_rng(22)
     layout = np.concatenate([np.full(128, 0), np.full(128, 7), np.full(128, -3), np.full(128, 1)]).astype(np.int32)
@@ -85,6 +101,8 @@ def test_out_of_range_expert_ids_are_padding():
     ([0, 1, 127, 128, 129, 200], 200, 256, 256, "bf16"),   # M_max not a multiple of 128
     ([300, 0, 512], 512, 384, 384, "f16"),
     ([-5, 700, 64], 256, 512, 128, "bf16"),                 # clamped into [0, M_max]
+    ([130, 5, 77], 130, 512, 256, "bf16"),                  # M_max % 4 != 0: byte-wise A scales
+    ([3, 0, 201], 201, 256, 384, "f16"),
 ])
 def test_small_masked(masked_m, Mmax, N, K, out):
     x = wl.small_masked(Mmax + N + K, masked_m, Mmax, N, K)
