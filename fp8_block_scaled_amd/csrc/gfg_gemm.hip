@@ -75,17 +75,19 @@ __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)
 // adjacent scale bytes), and this key keeps those reads conflict-free.
 __device__ __forceinline__ int swz_a(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 7)) << 4); }
 
+// Candidate 128-row tile c: is it computed, and its auxiliary value (the
+// tile's expert for the contiguous layout, its valid rows for the masked one).
 template <bool MASKED>
-__device__ __forceinline__ bool cand_valid(const Params& p, int c, int* g_out) {
+__device__ __forceinline__ bool cand_valid(const Params& p, int c, int* aux) {
     if (MASKED) {
         const int g = c / p.mt_per_group, j = c - g * p.mt_per_group;
         int mm = p.meta[g];
         mm = mm < 0 ? 0 : (mm > p.rows ? int(p.rows) : mm);
-        *g_out = g;
-        return j * BM < mm;
+        *aux = min(BM, mm - j * BM);
+        return *aux > 0;
     } else {
         const int g = p.meta[int64_t(c) * BM];
-        *g_out = g;
+        *aux = g;
         return g >= 0 && g < p.G;
     }
 }
@@ -110,14 +112,15 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
     return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
 }
 
-// The 4-byte word holding scale byte kb of a row, read as one global dword
-// (the byte is extracted where it is used, so no zero-extension of a freshly
-// loaded register forces a wait).  An aligned word that contains a byte of an
-// allocation lies in the same page as that byte, so the read never touches
-// unmapped memory.
-typedef const __attribute__((address_space(1))) uint32_t gword_t;
+// The 4-byte word holding scale byte kb of a wave's scale_b row, read through
+// the scalar data cache into a scalar register (the byte is extracted where it
+// is used).  A scalar load is counted by lgkmcnt, which every K-step drains
+// anyway, so it never makes the compiler wait on the vector-memory counter
+// (and with it on the LDS DMA in flight).  An aligned word that contains a
+// byte of an allocation lies in the same page as that byte.
+typedef const __attribute__((address_space(4))) uint32_t sword_t;
 __device__ __forceinline__ int load_scale_word(const uint8_t* row, int kb) {
-    return int(*reinterpret_cast<gword_t*>(reinterpret_cast<uintptr_t>(row + kb) & ~uintptr_t(3)));
+    return int(*reinterpret_cast<sword_t*>(reinterpret_cast<uintptr_t>(row + kb) & ~uintptr_t(3)));
 }
 __device__ __forceinline__ int scale_byte(int word, const uint8_t* row, int kb) {
     return (word >> (8 * int((reinterpret_cast<uintptr_t>(row) + uintptr_t(kb)) & 3))) & 0xff;
@@ -137,10 +140,10 @@ struct TileCtx {
     static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
     static constexpr int A_DMA = A_BYTES / 1024 / WAVES;   // 1 KB LDS-DMA wave instructions per stage
     static constexpr int B_DMA = B_BYTES / 1024 / WAVES;
-    // vector-memory loads one wave issues per stage: DMAs, the A scales (one
-    // dword or FM bytes) and the B-scale dword
+    // vector-memory loads one wave issues per stage: DMAs and the A scales (one
+    // dword or FM bytes); the B-scale dword is a scalar load
     static constexpr int SA_LOADS = SAW ? 1 : FM;
-    static constexpr int LOADS = A_DMA + B_DMA + SA_LOADS + 1;
+    static constexpr int LOADS = A_DMA + B_DMA + SA_LOADS;
 
     // Buffer resources (scalar registers): base + byte count.  The hardware
     // returns zero for any offset past the count instead of touching memory.
@@ -314,7 +317,7 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
         sb = load_scale_word(c.sb_row, kb_refill);
     }
     sched_pattern<0, C::FN * C::FM, ISSUE ? C::A_DMA + C::B_DMA : 0, READ ? 2 * (C::FM + C::FN) : 0,
-                  ISSUE ? C::SA_LOADS + 1 : 0>();
+                  ISSUE ? C::SA_LOADS : 0>();
     if (READ) cur = nxt;
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -332,35 +335,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
     __shared__ __attribute__((aligned(1024))) uint8_t smem1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem2[C::STAGE];
     __shared__ uint16_t tile_list[MT_MAX];   // valid candidate 128-row tiles, ascending
-    __shared__ int wave_count[NTHREADS / 64];
-    __shared__ int s_total;
+    __shared__ uint16_t tile_aux[MT_MAX];    // contiguous: the tile's expert; masked: its valid rows
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
 
     // ---- 1. compact the valid 128-row tiles (order preserved) --------------
-    if (tid == 0) s_total = 0;
+    // (the scan's counters sit in stage buffer 0, unused until the first DMA)
+    GFG_LDS int* const wave_count = reinterpret_cast<GFG_LDS int*>((GFG_LDS uint8_t*)smem0);
+    GFG_LDS int* const s_total = wave_count + NTHREADS / 64;
+    if (tid == 0) *s_total = 0;
     __syncthreads();
     for (int base = 0; base < p.n_cand; base += NTHREADS) {
         const int cnd = base + tid;
-        int g = -1;
-        const bool v = cnd < p.n_cand && cand_valid<MASKED>(p, cnd, &g);
+        int aux = 0;
+        const bool v = cnd < p.n_cand && cand_valid<MASKED>(p, cnd, &aux);
         const uint64_t bal = __ballot(v);
         const int before = __popcll(bal & ((uint64_t(1) << lane) - 1));
         if (lane == 0) wave_count[wave] = __popcll(bal);
         __syncthreads();
-        int off = s_total;
+        int off = *s_total;
         for (int w = 0; w < wave; ++w) off += wave_count[w];
-        if (v) tile_list[off + before] = uint16_t(cnd);
+        if (v) {
+            tile_list[off + before] = uint16_t(cnd);
+            tile_aux[off + before] = uint16_t(aux);
+        }
         __syncthreads();
         if (tid == 0) {
             int sum = 0;
             for (int w = 0; w < NTHREADS / 64; ++w) sum += wave_count[w];
-            s_total += sum;
+            *s_total += sum;
         }
         __syncthreads();
     }
-    const int n_mtiles = __builtin_amdgcn_readfirstlane(s_total);
+    const int n_mtiles = __builtin_amdgcn_readfirstlane(*s_total);
+    __syncthreads();   // every wave has read the counters before the DMA reuses their buffer
     const int NT = p.N / BN;
     const unsigned T = unsigned(n_mtiles) * unsigned(NT);
 
@@ -392,6 +401,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         const int nt = int(in_grp / gsz);
 
         const int cand = __builtin_amdgcn_readfirstlane(int(tile_list[r_rank]));
+        const int aux = __builtin_amdgcn_readfirstlane(int(tile_aux[r_rank]));
         int g;
         int64_t m0;             // first row of the tile inside its region
         const uint8_t* a_reg;   // region base (rows x K)
@@ -404,11 +414,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             a_reg = p.a + int64_t(g) * p.rows * p.K;
             sa_reg = p.a_scale + int64_t(g) * KB * p.rows;
             d_reg = reinterpret_cast<uint8_t*>(p.d) + int64_t(g) * p.rows * p.N * int64_t(sizeof(OutT));
-            int mm = p.meta[g];
-            mlimit = mm < 0 ? 0 : (mm > p.rows ? int(p.rows) : mm);
+            mlimit = int(m0) + aux;
         } else {
             m0 = int64_t(cand) * BM;
-            g = __builtin_amdgcn_readfirstlane(p.meta[m0]);
+            g = aux;
             a_reg = p.a;
             sa_reg = p.a_scale;
             d_reg = reinterpret_cast<uint8_t*>(p.d);
@@ -470,6 +479,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         Frags<BN> fa, fb;
         int sa0[4], sa1[4], sa2[4], sb0 = 0, sb1 = 0, sb2 = 0;
 
+        // Contiguous layout: the expert of each of this lane's four output rows
+        // (4*l16 + y, consecutive grouped_layout entries), read now so that the
+        // epilogue does not wait on a load.  The read goes through a buffer
+        // resource over the tile's valid rows: entries past them read as 0,
+        // and such rows fail the row < mlimit test anyway.
+        u32x4 lay = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (!MASKED) {
+            const int rv = int(min(int64_t(BM), p.rows - m0));
+            const __amdgpu_buffer_rsrc_t mr = make_rsrc(p.meta + m0, uint32_t(rv) * 4u);
+            lay = __builtin_amdgcn_raw_buffer_load_b128(mr, uint32_t(wm * 64 + 4 * l16) * 4u, 0, 0);
+        }
+
         // prologue: stages 0..2 in flight (clamped to the last stage), stage 0's
         // fragments in `fa`
         issue_stage(c, buf0, 0, wave, sa0, sb0);
@@ -497,11 +518,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         // ---- epilogue: lane owns row (4*l16 + y), columns 16x + 4lq .. +3 ----
 #pragma unroll
         for (int y = 0; y < FM; ++y) {
-            const int64_t row = m0 + wm * 64 + 4 * l16 + y;
-            bool ok = row < mlimit;
-            if (!MASKED && ok) ok = p.meta[row] == g;
+            const int row = int(m0) + wm * 64 + 4 * l16 + y;   // rows of a region fit in 32 bits
+            const bool ok = row < mlimit && (MASKED || int(lay[y]) == g);
             if (!ok) continue;
-            OutT* drow = reinterpret_cast<OutT*>(d_reg) + row * p.N + n0 + wn * WN + 4 * lq;
+            OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * p.N + n0 + wn * WN + 4 * lq;
 #pragma unroll
             for (int x = 0; x < FN; ++x) {
                 typedef OutT out4 __attribute__((ext_vector_type(4)));
