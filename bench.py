@@ -145,6 +145,83 @@ def cpu_baseline(w, x):
                       f"{dt:.2f} s; quantization untimed"}
 
 
+def quant_bytes(G, M, K, in_size):
+    """Algorithmic HBM bytes of one device quantizer call: read x, write the
+    E4M3 codes and the E8M0 scale bytes."""
+    return G * M * K * (in_size + 1) + G * M * (K // 128)
+
+
+def bench_quant(args):
+    """The device activation quantizer on a workload's A operand (bf16 or f32
+    input), timed with HIP events on its stream; HBM-bound, priced against
+    8 TB/s on algorithmic bytes."""
+    import torch
+    import fp8_block_scaled_amd as gfg
+    from fp8_block_scaled_amd import workloads as wl
+    from oracle import fp8_oracle as o
+
+    gfg.load_library()
+    w = wl.workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if args.in_dtype == "bf16" else torch.float32
+    in_size = 2 if args.in_dtype == "bf16" else 4
+    x0 = wl.draw(w)["a"]
+    if x0.ndim == 2:
+        x0 = x0[None]
+    G, M, K = x0.shape
+    per_set = quant_bytes(G, M, K, in_size)
+    nsets = args.sets or max(2, -(-(600 << 20) // per_set))
+    xs, qs, ss = [], [], []
+    for s in range(nsets):
+        x = x0 if s == 0 else wl.draw(w, seed_offset=s)["a"].reshape(G, M, K)
+        xs.append(torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt))
+        qs.append(torch.empty((G, M, K), dtype=torch.uint8, device=dev))
+        ss.append(torch.empty((G, K // 128, M), dtype=torch.uint8, device=dev))
+    code = gfg.IN_BF16 if dt == torch.bfloat16 else gfg.IN_F32
+    handle = torch.cuda.current_stream(dev).cuda_stream
+    calls = [(xs[i].data_ptr(), code, G, M, K, qs[i].data_ptr(), ss[i].data_ptr(), handle) for i in range(nsets)]
+
+    def step(i):
+        rc = gfg.raw_quantize_act_device(*calls[i % nsets])
+        if rc:
+            raise gfg.GfgError(rc, gfg.load_library().gfg_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize(dev)
+    ms = start.elapsed_time(stop) / args.steps
+    gbs = per_set / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "device activation quantizer GB/s (algorithmic bytes), 1 MI355X",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{args.in_dtype}->e4m3", "data": "synthetic",
+        "config": {"workload": f"quant_act_1x128 of {w.name}.a", "G": G, "M": M, "K": K,
+                   "in": args.in_dtype, "input_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "algorithmic_bytes_per_step": per_set,
+    }
+    if not args.no_cpu:
+        rows = min(M, 8192)
+        xs0 = xs[0][0, :rows].float().cpu().numpy()
+        t0 = time.perf_counter()
+        o.quantize_act_1x128(xs0)
+        dtc = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(quant_bytes(1, rows, K, in_size) / dtc / 1e9, 3), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"oracle quantize_act_1x128 on the first {rows} rows of group 0 "
+                                         f"({rows}x{K}), {dtc:.2f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,7 +238,16 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
                          "'bench.py --copy-bytes B' into profiles/traffic_<workload>.json, then exit")
+    ap.add_argument("--op", choices=("gemm", "quant"), default="gemm",
+                    help="gemm: the grouped GEMM (the default); quant: the device activation quantizer "
+                         "on the workload's A operand")
+    ap.add_argument("--in-dtype", choices=("bf16", "f32"), default="bf16", help="--op quant input dtype")
     args = ap.parse_args()
+    if args.op == "quant":
+        if args.gpus != 1:
+            raise SystemExit("this benchmark runs on one GPU only")
+        bench_quant(args)
+        return
     if args.traffic_from:
         if not args.copy_bytes:
             raise SystemExit("--traffic-from needs the --copy-bytes the counter runs used")

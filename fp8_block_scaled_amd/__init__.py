@@ -1,9 +1,10 @@
 """Grouped FP8 (E4M3) block-scaled GEMM for MI355X (gfx950).
 
 A thin ctypes binding over ``libgfg.so`` (declared in ``include/gfg.h``):
-argument marshalling only.  Every step of the GEMM runs in the library's HIP
-kernels; the quantizers run in the library's C++ host code.  There is no
-fallback: if the library is missing or fails to load, every call raises.
+argument marshalling only.  Every step of the GEMM and of the device
+quantizer runs in the library's HIP kernels; the host quantizers run in the
+library's C++ host code.  There is no fallback: if the library is missing or
+fails to load, every call raises.
 
 The operations are the two DeepGEMM-style grouped ops described on the first
 reference page, "Grouped and Batched GEMM kernels with blockscaling matching
@@ -21,11 +22,13 @@ import numpy as np
 __all__ = [
     "GfgError", "load_library", "grouped_fp8_gemm_contiguous", "grouped_fp8_gemm_masked",
     "fp8_quantize_act_1x128", "fp8_quantize_weight_128x128", "fp8_quantize_act_masked",
-    "raw_contiguous", "raw_masked", "OUT_BF16", "OUT_F16",
+    "fp8_quantize_act_1x128_device", "raw_contiguous", "raw_masked", "raw_quantize_act_device",
+    "OUT_BF16", "OUT_F16", "IN_F32", "IN_BF16",
 ]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgfg.so")
 OUT_BF16, OUT_F16 = 0, 1
+IN_F32, IN_BF16 = 0, 1
 _STATUS = {0: "GFG_OK", 1: "GFG_EINVAL", 2: "GFG_EUNSUPPORTED", 3: "GFG_EHIP", 4: "GFG_ERANGE"}
 _lib = None
 
@@ -54,6 +57,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_quantize_act_1x128.restype = ctypes.c_int
     lib.fp8_quantize_weight_128x128.argtypes = [vp, i32, i64, i64, vp, vp]
     lib.fp8_quantize_weight_128x128.restype = ctypes.c_int
+    lib.fp8_quantize_act_1x128_device.argtypes = [vp, i32, i32, i64, i64, vp, vp, vp]
+    lib.fp8_quantize_act_1x128_device.restype = ctypes.c_int
     lib.gfg_last_error.argtypes = []
     lib.gfg_last_error.restype = ctypes.c_char_p
     lib.gfg_version.argtypes = []
@@ -78,6 +83,10 @@ def raw_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out_dt
 def raw_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, stream=0) -> int:
     return load_library().grouped_fp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d,
                                                   G, M_max, N, K, out_dtype, stream)
+
+
+def raw_quantize_act_device(x, in_dtype, G, M, K, q, scale_t, stream=0) -> int:
+    return load_library().fp8_quantize_act_1x128_device(x, in_dtype, G, M, K, q, scale_t, stream)
 
 
 # ------------------------------------------------------------------ torch-facing calls
@@ -162,6 +171,35 @@ def grouped_fp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d, stream=None):
         _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev),
         G, Mmax, N, K, _out_code(d), _stream_handle(stream, dev)))
     return d
+
+
+def fp8_quantize_act_1x128_device(x, q=None, scale_t=None, stream=None):
+    """Per-token (1,128) ceil-E8M0 quantization on the GPU (asynchronous on ``stream``).
+
+    x [M, K] or [G, M, K] float32 or bfloat16 on a GPU, K a multiple of 128 ->
+    (q uint8 e4m3 codes of x's shape, scale_t uint8 [ceil(K/128), M] or
+    [G, ceil(K/128), M]).  ``q`` and ``scale_t`` may be passed in (contiguous
+    uint8 / float8_e4m3fn tensors of those shapes on x's device); otherwise
+    they are allocated here with torch.
+    """
+    torch = _torch()
+    dev = x.device
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [M, K] or [G, M, K]")
+    G, M, K = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
+    lead = () if x.dim() == 2 else (G,)
+    if q is None:
+        q = torch.empty(tuple(x.shape), dtype=torch.uint8, device=dev)
+    if scale_t is None:
+        scale_t = torch.empty(lead + (-(-K // 128), M), dtype=torch.uint8, device=dev)
+    if tuple(q.shape) != tuple(x.shape) or tuple(scale_t.shape) != lead + (-(-K // 128), M):
+        raise ValueError("q / scale_t shapes do not match x")
+    code = IN_F32 if x.dtype == torch.float32 else IN_BF16
+    _check(raw_quantize_act_device(
+        _dev_ptr(x, "x", (torch.float32, torch.bfloat16), dev), code, G, M, K,
+        _dev_ptr(q, "q", (torch.uint8, torch.float8_e4m3fn), dev),
+        _dev_ptr(scale_t, "scale_t", (torch.uint8,), dev), _stream_handle(stream, dev)))
+    return q, scale_t
 
 
 # ------------------------------------------------------------------ host quantizers

@@ -38,10 +38,13 @@ def build(verbose: bool = False) -> str:
     steps = [
         [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "gfg_gemm.hip"),
          "-o", os.path.join(out_dir, "gfg_gemm.o")],
+        [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "gfg_quant.hip"),
+         "-o", os.path.join(out_dir, "gfg_quant.o")],
         ["g++", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-pthread", "-I", INCLUDE, "-I", CSRC, "-c",
          os.path.join(CSRC, "gfg_host.cpp"), "-o", os.path.join(out_dir, "gfg_host.o")],
     ]
-    objs = [os.path.join(out_dir, "gfg_gemm.o"), os.path.join(out_dir, "gfg_host.o")]
+    objs = [os.path.join(out_dir, "gfg_gemm.o"), os.path.join(out_dir, "gfg_quant.o"),
+            os.path.join(out_dir, "gfg_host.o")]
     tmp = LIB + ".tmp"
     steps.append([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp])
     for cmd in steps:

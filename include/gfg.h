@@ -54,6 +54,7 @@ enum gfg_status {
 };
 
 enum gfg_out_dtype { GFG_OUT_BF16 = 0, GFG_OUT_F16 = 1 };
+enum gfg_in_dtype { GFG_IN_F32 = 0, GFG_IN_BF16 = 1 };
 
 /*
  * Contiguous grouped GEMM (the DeepGEMM-style m_grouped ... contiguous op).
@@ -119,6 +120,33 @@ GFG_API int fp8_quantize_act_1x128(const float* x, int64_t M, int64_t K,
                            uint8_t* q, uint8_t* scale_t);
 GFG_API int fp8_quantize_weight_128x128(const float* w, int32_t G, int64_t N, int64_t K,
                                 uint8_t* q, uint8_t* scale);
+
+/*
+ * Device quantizer (GPU, asynchronous on `stream`): the activation quantizer
+ * above, run on the device, producing the A operand of either GEMM layout.
+ *
+ *   x        [G][M][K]            float32 (in_dtype GFG_IN_F32) or bfloat16
+ *                                 (GFG_IN_BF16), DEVICE memory, 16-byte aligned
+ *   q        [G][M][K]            e4m3 bytes, DEVICE memory, 16-byte aligned
+ *   scale_t  [G][K/128][M]        E8M0 bytes, DEVICE memory (the transposed
+ *                                 per-token layout, per group)
+ *
+ * G = 1 gives the contiguous layout's a / a_scale; G groups of M = M_max rows
+ * give the masked layout's.  Per (1,128) block: t = the smallest integer with
+ * 448 * 2^t >= max|x| (t = 0 for an all-zero block), scale byte t + 127,
+ * q = E4M3(x / 2^t) nearest-even, as in the host quantizer (first reference
+ * page, sections "Summary" and "DeepGEMM conformance details").  Where the
+ * host quantizer returns GFG_ERANGE the device one cannot stop; instead a
+ * block with a NaN or infinity gets scale byte 255 (E8M0 NaN) and q = 0x7F
+ * (E4M3 NaN) for all its elements, and a block so small that t < -127 gets
+ * t = -127 (which still keeps |x / 2^t| <= 448).
+ *
+ * Sizes: G in [1, 65535]; M, K >= 0 (either 0 is a no-op); K a multiple of
+ * 128 and M, K <= 2^30 (else GFG_EUNSUPPORTED).  The library allocates and
+ * synchronizes nothing.
+ */
+GFG_API int fp8_quantize_act_1x128_device(const void* x, int32_t in_dtype, int32_t G, int64_t M, int64_t K,
+                                          uint8_t* q, uint8_t* scale_t, void* stream);
 
 /* Thread-local message describing the calling thread's last failure ("" if none). */
 GFG_API const char* gfg_last_error(void);

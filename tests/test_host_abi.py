@@ -112,6 +112,20 @@ def test_quantizer_argument_errors():
     assert lib.fp8_quantize_weight_128x128(None, 0, 128, 128, None, None) == 1
 
 
+def test_device_quantizer_argument_errors():
+    # host-side checks that return before any HIP call (fake addresses are never touched)
+    q = gfg.raw_quantize_act_device
+    assert q(0x1000, 2, 1, 4, 128, 0x1000, 0x1000) == 1          # bad in_dtype
+    assert q(0x1000, 0, 0, 4, 128, 0x1000, 0x1000) == 1          # G = 0
+    assert q(0x1000, 0, 1, -1, 128, 0x1000, 0x1000) == 1         # negative M
+    assert q(None, 0, 1, 0, 128, None, None) == 0                # empty: no-op
+    assert q(None, 1, 1, 4, 0, None, None) == 0
+    assert q(None, 0, 1, 4, 128, 0x1000, 0x1000) == 1            # null x
+    assert q(0x1000, 0, 1, 4, 200, 0x1000, 0x1000) == 2          # K not a multiple of 128
+    assert q(0x1008, 0, 1, 4, 128, 0x1000, 0x1000) == 1          # x not 16-byte aligned
+    assert "16-byte" in gfg.load_library().gfg_last_error().decode()
+
+
 # Host-side argument checks of the GEMM entry points: these return before any
 # HIP call, so fake non-null addresses are never dereferenced.
 FAKE = 0x1000
