@@ -83,14 +83,27 @@ def standard_workloads() -> list[Workload]:
     return ws
 
 
+def context_workloads() -> list[Workload]:
+    """Shapes outside the five reference workloads, measured for context.
+
+    ``dense_g1_m4096_n4096_k16384``: one group, a plain 4096 x 4096 x 16384
+    block-scaled GEMM, the shape at which the second reference page
+    ("[Kernel][MI350] cache-aware 8-wave BF16/FP16 GEMM", section "Perf", its
+    first table) quotes an FP8 dense throughput (row-scaled there, on another
+    power profile; block-scaled here).  A, B ~ N(0, 1), seed 1005.
+    """
+    return [Workload("dense_g1_m4096_n4096_k16384", "contiguous", 1, 4096, 16384, "bf16", 1005,
+                     m_per_group=[4096])]
+
+
 def workload(name_or_index) -> Workload:
-    """A standard workload by index or name, or an ad-hoc one named
-    ``contig_g{G}_m{rows per group}_n{N}_k{K}`` or ``masked_g{G}_m{M_max}_n{N}_k{K}``
-    (every group full; bf16 out; seed 2000)."""
+    """A standard workload by index or name, a context workload by name, or an
+    ad-hoc one named ``contig_g{G}_m{rows per group}_n{N}_k{K}`` or
+    ``masked_g{G}_m{M_max}_n{N}_k{K}`` (every group full; bf16 out; seed 2000)."""
     ws = standard_workloads()
     if isinstance(name_or_index, int):
         return ws[name_or_index]
-    for w in ws:
+    for w in ws + context_workloads():
         if w.name == name_or_index:
             return w
     import re

@@ -44,7 +44,7 @@ def _cols(col_blocks):
     return np.concatenate([np.arange(128 * c, 128 * c + 128) for c in col_blocks])
 
 
-@pytest.mark.parametrize("idx", [1, 2, 4])
+@pytest.mark.parametrize("idx", [1, 2, 4, "dense_g1_m4096_n4096_k16384"])
 def test_contiguous_workload_full_size(idx):
     w = wl.workload(idx)
     print(f"[workload] {w.name} M={w.M} N={w.N} K={w.K} G={w.G}", flush=True)
