@@ -70,10 +70,16 @@ struct Params {
 // per row covering its 8 chunks).
 __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 4); }
 
-// The A tile's swizzle keys on (r >> 2) & 7 instead: an A fragment takes rows
-// 4 apart (row 4*l16 + f of the wave's 64, so that a lane's four rows have
-// adjacent scale bytes), and this key keeps those reads conflict-free.
-__device__ __forceinline__ int swz_a(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 7)) << 4); }
+// The A tile is laid out differently: an A fragment takes rows 4 apart (row
+// 4*l16 + f of the wave's 64, so that a lane's four rows have adjacent scale
+// bytes).  Sixteen such rows all have the same row parity, and the parity
+// picks the half of the 64 four-byte banks a 128-byte row falls in, so a plain
+// layout reads them with two-way bank conflicts (measured: half the LDS read
+// rate).  LDS row p therefore holds A row a_row(p) = p ^ ((p >> 2) & 1), which
+// moves every other lane's rows to the other half, and the 16-byte chunks are
+// XOR-swizzled with (p >> 2) & 7.  Measured conflict-free at the full rate.
+__device__ __forceinline__ int a_row(int p) { return p ^ ((p >> 2) & 1); }   // an involution
+__device__ __forceinline__ int swz_a(int p, int c) { return p * BK + ((c ^ ((p >> 2) & 7)) << 4); }
 
 // Candidate 128-row tile c: is it computed, and its auxiliary value (the
 // tile's expert for the contiguous layout, its valid rows for the masked one).
@@ -155,9 +161,10 @@ struct TileCtx {
     uint32_t a_off[A_DMA];     // per-lane source offsets of this wave's DMA chunks
     uint32_t b_off[B_DMA];
     uint32_t sa_off[4];        // A-scale byte offsets (SAW: [0] only, the dword)
-    // LDS byte offsets of this lane's fragment row, logical chunks lq (lo) and
-    // lq + 4 (hi); with the XOR swizzle the hi chunk sits at lo ^ 64.
-    int a_lo, a_hi, b_lo, b_hi;
+    // LDS byte offsets of this lane's fragment rows, logical chunks lq (lo) and
+    // lq + 4 (hi).  A fragment y sits at a_*_e + y*BK for even y and at
+    // a_*_o + y*BK for odd y (the row-parity exchange of the A layout).
+    int a_lo_e, a_lo_o, a_hi_e, a_hi_o, b_lo, b_hi;
 };
 
 template <int BN>
@@ -214,8 +221,8 @@ __device__ __forceinline__ void read_frags(const C& c, const GFG_LDS uint8_t* __
                                            Frags<C::BN>& f) {
 #pragma unroll
     for (int y = 0; y < C::FM; ++y) {
-        const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + c.a_lo + y * BK);
-        const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + c.a_hi + y * BK);
+        const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + ((y & 1) ? c.a_lo_o : c.a_lo_e) + y * BK);
+        const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + ((y & 1) ? c.a_hi_o : c.a_hi_e) + y * BK);
         f.a[y] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
@@ -300,8 +307,8 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
     if (READ) {
 #pragma unroll
         for (int y = 0; y < C::FM; ++y) {
-            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + c.a_lo + y * BK);
-            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + c.a_hi + y * BK);
+            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + ((y & 1) ? c.a_lo_o : c.a_lo_e) + y * BK);
+            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + ((y & 1) ? c.a_hi_o : c.a_hi_e) + y * BK);
             nxt.a[y] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
@@ -438,9 +445,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             const int rr = lane >> 3, pc = lane & 7;
 #pragma unroll
             for (int j = 0; j < C::A_DMA; ++j) {
-                const int r = 8 * (j * C::WAVES + wave) + rr;
-                const int lc = pc ^ ((r >> 2) & 7);
-                int64_t row = m0 + r;
+                const int pr = 8 * (j * C::WAVES + wave) + rr;    // LDS row
+                const int lc = pc ^ ((pr >> 2) & 7);
+                int64_t row = m0 + a_row(pr);
                 row = row < mlimit ? row : mlimit - 1;           // clamp: never read outside
                 c.a_off[j] = uint32_t(row - m0) * uint32_t(p.K) + uint32_t(lc * 16);
             }
@@ -462,11 +469,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
                 c.sa_off[f] = uint32_t(row - m0);
             }
         }
-        // fragment rows: A row wm*64 + 4*l16 + y (swizzle key l16 & 7 for every
-        // y, so fragment y sits y rows below fragment 0), B row wn*WN + x*16 + l16
-        // (key l16 & 7).
-        c.a_lo = swz_a(wm * 64 + 4 * l16, lq);
-        c.a_hi = swz_a(wm * 64 + 4 * l16, lq + 4);
+        // fragment rows: A row wm*64 + 4*l16 + y lives in LDS row p0 + (y ^ odd)
+        // with p0 = wm*64 + 4*l16 and odd = l16 & 1 (swizzle key l16 & 7 for
+        // every y); B row wn*WN + x*16 + l16 (key l16 & 7).
+        {
+            const int p0 = wm * 64 + 4 * l16, odd = l16 & 1;
+            c.a_lo_e = swz_a(p0, lq) + odd * BK;          // even y: row p0 + odd + y
+            c.a_lo_o = swz_a(p0, lq) - odd * BK;          // odd y: row p0 - odd + y
+            c.a_hi_e = swz_a(p0, lq + 4) + odd * BK;
+            c.a_hi_o = swz_a(p0, lq + 4) - odd * BK;
+        }
         c.b_lo = swz(wn * WN + l16, lq);
         c.b_hi = swz(wn * WN + l16, lq + 4);
 
