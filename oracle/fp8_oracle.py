@@ -233,6 +233,60 @@ def quantize_act_masked(x: np.ndarray):
     return np.stack(qs), np.stack(ss)
 
 
+# ---------------------------------------------------------------- gemm1 + silu_mul
+# The expert MLP's first GEMM projects each token to a gate half and an up
+# half and multiplies silu(gate) into up (page 3, the RadeonFlow pull request
+# "flydsl mxfp4 a4w4 MoE: bring gemm1/gemm2 to parity with the HIP backend",
+# section "Changes", item gemm1: the silu_mul epilogue, with the exponential
+# taken by the hardware base-2 exponential).  Readings of what the page leaves
+# open: B[g] holds 2*I rows, rows [0, I) the gate projection and rows [I, 2*I)
+# the up projection; silu(x) = x / (1 + e**-x); out = silu(gate) * up, an
+# [M, I] (or [G, M_max, I]) result over the same valid rows as the GEMM.
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """silu(x) = x / (1 + exp(-x)), float64 (x * logistic sigmoid of x)."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def _silu_mul_rows(d: np.ndarray) -> np.ndarray:
+    """[..., 2I] gate|up → [..., I] silu(gate) * up."""
+    half = d.shape[-1] // 2
+    return silu(d[..., :half]) * d[..., half:]
+
+
+def grouped_gemm_silu_mul_contiguous(q_a, scale_a, q_b, scale_b, grouped_layout, out_init=None):
+    """Contiguous gemm1 with silu_mul, float64.
+
+    q_b is [G, 2I, K].  For each expert g and each row with
+    ``grouped_layout == g``: ``h = A_dq[row] @ B_dq[g]^T`` (length 2I) and
+    ``out[row] = silu(h[:I]) * h[I:]``.  Padding rows keep ``out_init`` (NaN
+    when none is given).
+    """
+    d = grouped_gemm_contiguous(q_a, scale_a, q_b, scale_b, grouped_layout)
+    M, half = d.shape[0], d.shape[1] // 2
+    out = np.full((M, half), np.nan) if out_init is None else np.array(out_init, dtype=np.float64)
+    layout = np.asarray(grouped_layout, dtype=np.int64)
+    rows = np.nonzero((layout >= 0) & (layout < q_b.shape[0]))[0]
+    out[rows] = _silu_mul_rows(d[rows])
+    return out
+
+
+def grouped_gemm_silu_mul_masked(q_a, scale_a, q_b, scale_b, masked_m, out_init=None):
+    """Masked gemm1 with silu_mul, float64: rows ``m < masked_m[g]`` of group g
+    get ``silu(h[:I]) * h[I:]`` with ``h = A_dq[g, m] @ B_dq[g]^T``; other rows
+    keep ``out_init``."""
+    d = grouped_gemm_masked(q_a, scale_a, q_b, scale_b, masked_m)
+    G, Mmax, half = d.shape[0], d.shape[1], d.shape[2] // 2
+    out = np.full((G, Mmax, half), np.nan) if out_init is None else np.array(out_init, dtype=np.float64)
+    for g in range(G):
+        mm = int(min(max(int(masked_m[g]), 0), Mmax))
+        if mm:
+            out[g, :mm] = _silu_mul_rows(d[g, :mm])
+    return out
+
+
 # ---------------------------------------------------------------- metrics
 def calc_diff(x, y) -> float:
     """1 - 2*sum(x*y) / sum(x*x + y*y), in float64 ("cosine-similarity-style")."""

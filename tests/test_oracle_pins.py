@@ -441,3 +441,115 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         failures += 1
     monkeypatch.setattr(o, "grouped_gemm_masked", real_gm)
     assert failures == 7
+
+
+# ------------------------------------------------------------------ gemm1 + silu_mul pins
+def test_silu_closed_forms():
+    """silu against what mathematics fixes independently of its formula:
+    silu(0) = 0; silu(1) = 1/(1 + 1/e) and silu(-1) = silu(1) - 1 (printed
+    constants); the odd part silu(x) - silu(-x) = x; the tanh form
+    x * (1 + tanh(x/2)) / 2; scipy's logistic function; the limits at large |x|."""
+    import scipy.special
+    assert o.silu(np.array(0.0)) == 0.0
+    assert abs(float(o.silu(np.array(1.0))) - 0.7310585786300049) < 1e-15
+    assert abs(float(o.silu(np.array(-1.0))) + 0.2689414213699951) < 1e-15
+    x = np.linspace(-60.0, 60.0, 24001)
+    np.testing.assert_allclose(o.silu(x) - o.silu(-x), x, rtol=0, atol=1e-12)
+    # (1 + tanh) cancels for large negative x: an absolute bound there
+    np.testing.assert_allclose(o.silu(x), x * (1.0 + np.tanh(x / 2.0)) / 2.0, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o.silu(x), x * scipy.special.expit(x), rtol=1e-13, atol=1e-300)
+    big = np.array([-1000.0, -800.0, 800.0])
+    got = o.silu(big)
+    assert got[0] == 0.0 and got[1] == 0.0 and got[2] == 800.0
+
+
+def _tanh_silu(v: float) -> float:
+    return v * (1.0 + math.tanh(v / 2.0)) / 2.0
+
+
+def test_silu_mul_contiguous_bruteforce_tiny():
+    """Gate rows [0, I) and up rows [I, 2I) of each expert's B: every valid row
+    against an fsum triple loop and the tanh form of silu; padding rows keep
+    the initial buffer."""
+    rng = np.random.default_rng(21)
+    layout = np.array([1, 1, -1, 0, 0, 0, -1, 1], np.int32)
+    K, I = 256, 128
+    a = rng.standard_normal((layout.size, K)).astype(np.float32)
+    b = rng.standard_normal((2, 2 * I, K)).astype(np.float32)
+    qa, sa = o.quantize_act_1x128(a)
+    qb, sb = o.quantize_weight_128x128(b)
+    out0 = np.full((layout.size, I), 9.25)
+    out = o.grouped_gemm_silu_mul_contiguous(qa, sa, qb, sb, layout, out0)
+    assert out.shape == (layout.size, I)
+    for g in range(2):
+        rows = [r for r in range(layout.size) if layout[r] == g]
+        h = _bf_gemm_rows(qa, sa, qb, sb, rows, g)
+        for i, r in enumerate(rows):
+            for n in range(0, I, 7):
+                ref = _tanh_silu(h[i, n]) * h[i, I + n]
+                assert abs(out[r, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+    assert np.all(out[layout < 0] == 9.25)
+
+
+def test_silu_mul_masked_bruteforce_tiny():
+    rng = np.random.default_rng(22)
+    G, Mmax, K, I = 3, 5, 256, 128
+    a = rng.standard_normal((G, Mmax, K)).astype(np.float32)
+    b = rng.standard_normal((G, 2 * I, K)).astype(np.float32)
+    masked_m = np.array([2, 5, 0], np.int32)
+    qa, sa = o.quantize_act_masked(a)
+    qb, sb = o.quantize_weight_128x128(b)
+    out0 = np.full((G, Mmax, I), -1.5)
+    out = o.grouped_gemm_silu_mul_masked(qa, sa, qb, sb, masked_m, out0)
+    assert out.shape == (G, Mmax, I)
+    for g in range(G):
+        mm = int(masked_m[g])
+        if mm:
+            h = _bf_gemm_rows(qa[g], sa[g], qb, sb, list(range(mm)), g)
+            for m in range(mm):
+                for n in range(0, I, 11):
+                    ref = _tanh_silu(h[m, n]) * h[m, I + n]
+                    assert abs(out[g, m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+        assert np.all(out[g, mm:] == -1.5)
+
+
+def test_silu_mul_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible gemm1 mistakes in the oracle (on the CPU): gate and up
+    halves exchanged, the x factor of silu dropped (a bare sigmoid), and the
+    activation applied to every row including padding."""
+    failures = 0
+    real_rows = o._silu_mul_rows
+
+    def swapped(d):
+        half = d.shape[-1] // 2
+        return o.silu(d[..., half:]) * d[..., :half]
+    monkeypatch.setattr(o, "_silu_mul_rows", swapped)
+    try:
+        test_silu_mul_contiguous_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "_silu_mul_rows", real_rows)
+    real_silu = o.silu
+    monkeypatch.setattr(o, "silu", lambda x: 1.0 / (1.0 + np.exp(-np.asarray(x, np.float64))))
+    try:
+        test_silu_mul_masked_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "silu", real_silu)
+    real_gc = o.grouped_gemm_contiguous
+
+    def all_rows(qa, sa, qb, sb, layout, d_init=None):
+        return real_gc(qa, sa, qb, sb, np.where(np.asarray(layout) < 0, 0, layout), d_init)
+    monkeypatch.setattr(o, "grouped_gemm_contiguous", all_rows)
+    real_sc = o.grouped_gemm_silu_mul_contiguous
+
+    def silu_all_rows(qa, sa, qb, sb, layout, out_init=None):
+        return real_sc(qa, sa, qb, sb, np.where(np.asarray(layout) < 0, 0, layout), out_init)
+    monkeypatch.setattr(o, "grouped_gemm_silu_mul_contiguous", silu_all_rows)
+    try:
+        test_silu_mul_contiguous_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "grouped_gemm_contiguous", real_gc)
+    monkeypatch.setattr(o, "grouped_gemm_silu_mul_contiguous", real_sc)
+    assert failures == 3
