@@ -4,7 +4,8 @@
 
 A step is one call of the grouped GEMM (tile scheduling, LDS-staged scaled-MFMA
 K-loop and epilogue, all inside the one kernel) over one batch of seeded
-synthetic inputs already resident in HBM; quantization happens before timing,
+synthetic inputs already resident in HBM (for a gemm1 workload, such as
+kimi_tp4_gemm1_t4096, the call with the fused silu_mul epilogue); quantization happens before timing,
 as the inputs of the op are FP8 bytes and E8M0 scales.  Several input sets
 whose combined size exceeds the 256 MB Infinity Cache rotate between steps, so
 each step streams its operands from HBM.
@@ -29,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA peak
 PEAK_HBM_GBS = 8000.0
+RIDGE_FLOP_PER_BYTE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 DEFAULT_WORKLOAD = "contig_g4_m1024_n2048_k7168"
 KERNEL_SRC = os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", "gfg_gemm.hip")
 
@@ -48,6 +50,7 @@ def algorithmic_bytes(w, layout=None) -> int:
     experts that have rows, both scale tensors' used parts, and D's valid rows."""
     KB, NB = w.K // 128, w.N // 128
     out_b = 2
+    out_cols = w.I if w.op == "silu_mul" else w.N
     if w.layout == "masked":
         tiles_rows = sum(-(-min(max(m, 0), w.M_max) // 128) * 128 for m in w.masked_m)
         a_rows = sum(min(max(m, 0), w.M_max) for m in w.masked_m)
@@ -57,7 +60,7 @@ def algorithmic_bytes(w, layout=None) -> int:
         a_rows = w.M
         groups = sum(1 for m in w.m_per_group if m > 0)
     return int(a_rows * w.K + tiles_rows * KB + groups * (w.N * w.K + NB * KB)
-               + w.m_valid * w.N * out_b)
+               + w.m_valid * out_cols * out_b)
 
 
 def traffic_from_profile(w):
@@ -126,6 +129,23 @@ def cpu_baseline(w, x):
     the host.  Its own quantizer prepares the operands outside the timing."""
     from threadpoolctl import threadpool_info
     from oracle import fp8_oracle as o
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    if w.op == "silu_mul":
+        # bounded sample: the rows of the first 16 experts (the full weight set
+        # would be 22 GB in float64)
+        n_exp = min(16, w.G)
+        layout = x["grouped_layout"]
+        rows = np.nonzero((layout >= 0) & (layout < n_exp))[0]
+        qa, sa = o.quantize_act_1x128(x["a"][rows])
+        qb_d, sb_d = o.quantize_weight_128x128(x["b"])
+        sel = x["b_index"][:n_exp]
+        t0 = time.perf_counter()
+        o.grouped_gemm_silu_mul_contiguous(qa, sa, qb_d[sel], sb_d[sel], layout[rows])
+        dt = time.perf_counter() - t0
+        flops = 2 * rows.size * w.N * w.K
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"the rows of experts 0..{n_exp - 1} of {w.name} ({rows.size} of {w.m_valid} valid rows; "
+                          f"fp64 dequantize + matmul + silu_mul), {dt:.2f} s; quantization untimed"}
     if w.layout == "masked":
         qa, sa = o.quantize_act_masked(x["a"])
         qb, sb = o.quantize_weight_128x128(x["b"])
@@ -138,7 +158,6 @@ def cpu_baseline(w, x):
         t0 = time.perf_counter()
         o.grouped_gemm_contiguous(qa, sa, qb, sb, x["grouped_layout"])
         dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     return {"value": round(w.flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"one full step of {w.name} (fp64 dequantize + matmul over all valid rows), "
@@ -285,9 +304,14 @@ def main():
             meta = torch.from_numpy(x["grouped_layout"]).to(dev)
             M_rows = w.M
         qb, sb = gfg.fp8_quantize_weight_128x128(x["b"])
+        b_dev, sb_dev = torch.from_numpy(qb).to(dev), torch.from_numpy(sb).to(dev)
+        if w.b_distinct:      # every expert its own copy in device memory
+            idx = torch.from_numpy(x["b_index"]).to(dev)
+            b_dev, sb_dev = b_dev.index_select(0, idx), sb_dev.index_select(0, idx)
+        out_cols = w.I if w.op == "silu_mul" else w.N
         t = dict(a=torch.from_numpy(qa).to(dev), sa=torch.from_numpy(sa).to(dev),
-                 b=torch.from_numpy(qb).to(dev), sb=torch.from_numpy(sb).to(dev), meta=meta,
-                 d=torch.empty((M_rows, w.N), dtype=torch.bfloat16 if w.out_dtype == "bf16" else torch.float16,
+                 b=b_dev, sb=sb_dev, meta=meta,
+                 d=torch.empty((M_rows, out_cols), dtype=torch.bfloat16 if w.out_dtype == "bf16" else torch.float16,
                                device=dev))
         sets.append(t)
         if s:
@@ -299,14 +323,16 @@ def main():
     # prepared launches: pointers and sizes resolved once
     calls = []
     for t in sets:
+        silu = w.op == "silu_mul"
+        n_arg = w.I if silu else w.N      # the silu_mul entry points take I (B has 2*I rows)
         if w.layout == "masked":
             a = (t["a"].data_ptr(), t["sa"].data_ptr(), t["b"].data_ptr(), t["sb"].data_ptr(),
-                 t["meta"].data_ptr(), t["d"].data_ptr(), w.G, w.M_max, w.N, w.K, out_code, handle)
-            calls.append((gfg.raw_masked, a))
+                 t["meta"].data_ptr(), t["d"].data_ptr(), w.G, w.M_max, n_arg, w.K, out_code, handle)
+            calls.append((gfg.raw_silu_mul_masked if silu else gfg.raw_masked, a))
         else:
             a = (t["a"].data_ptr(), t["sa"].data_ptr(), t["b"].data_ptr(), t["sb"].data_ptr(),
-                 t["meta"].data_ptr(), t["d"].data_ptr(), w.M, w.N, w.K, w.G, out_code, handle)
-            calls.append((gfg.raw_contiguous, a))
+                 t["meta"].data_ptr(), t["d"].data_ptr(), w.M, n_arg, w.K, w.G, out_code, handle)
+            calls.append((gfg.raw_silu_mul_contiguous if silu else gfg.raw_contiguous, a))
 
     def step(i):
         fn, a = calls[i % len(calls)]
@@ -328,6 +354,14 @@ def main():
     ms = start.elapsed_time(stop) / args.steps
     tflops = w.flops / (ms * 1e-3) / 1e12
     traffic = traffic_from_profile(w)
+    abytes = algorithmic_bytes(w)
+    gbps = abytes / (ms * 1e-3) / 1e9
+    if w.flops / abytes >= RIDGE_FLOP_PER_BYTE:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP8_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+    else:   # below the ridge the algorithmic bytes bound the step
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": traffic}
 
     res = {
         "metric": "grouped FP8 GEMM TFLOP/s (valid rows) and % of FP8 MFMA peak, 1 MI355X",
@@ -342,15 +376,13 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8e4m3",
         "data": "synthetic",
-        "config": {"workload": w.name, "layout": w.layout, "G": w.G, "N": w.N, "K": w.K,
+        "config": {"workload": w.name, "op": w.op, "layout": w.layout, "G": w.G, "N": w.N, "K": w.K,
                    "M_rows": w.M, "M_valid": w.m_valid, "out": w.out_dtype,
                    "input_sets": nsets, "parallelism": "none (1 GPU)"},
         "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": traffic},
-        "algorithmic_bytes_per_step": algorithmic_bytes(w),
-        "algorithmic_GBps": round(algorithmic_bytes(w) / (ms * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "algorithmic_bytes_per_step": abytes,
+        "algorithmic_GBps": round(gbps, 1),
         "host_wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu:

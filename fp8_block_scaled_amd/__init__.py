@@ -11,6 +11,9 @@ reference page, "Grouped and Batched GEMM kernels with blockscaling matching
 DeepGEMM API": a contiguous layout (``grouped_layout`` maps rows to experts,
 -1 marks padding) and a masked layout (``[G, M_max, K]`` with ``masked_m``),
 FP8 E4M3 operands with (1,128) activation and (128,128) weight E8M0 scales.
+Both layouts also come as gemm1 of the expert MLP with its silu_mul epilogue
+(third reference page, the MoE gemm1/gemm2 pull request, section "Changes"):
+``out = silu(gate) * up`` with gate and up the two halves of ``A . B[g]^T``.
 """
 from __future__ import annotations
 
@@ -23,6 +26,8 @@ __all__ = [
     "GfgError", "load_library", "grouped_fp8_gemm_contiguous", "grouped_fp8_gemm_masked",
     "fp8_quantize_act_1x128", "fp8_quantize_weight_128x128", "fp8_quantize_act_masked",
     "fp8_quantize_act_1x128_device", "raw_contiguous", "raw_masked", "raw_quantize_act_device",
+    "grouped_fp8_gemm_silu_mul_contiguous", "grouped_fp8_gemm_silu_mul_masked",
+    "raw_silu_mul_contiguous", "raw_silu_mul_masked",
     "OUT_BF16", "OUT_F16", "IN_F32", "IN_BF16",
 ]
 
@@ -53,6 +58,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.grouped_fp8_gemm_contiguous.restype = ctypes.c_int
     lib.grouped_fp8_gemm_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
     lib.grouped_fp8_gemm_masked.restype = ctypes.c_int
+    lib.grouped_fp8_gemm_silu_mul_contiguous.argtypes = [vp, u8p, vp, u8p, vp, vp, i64, i64, i64, i32, i32, vp]
+    lib.grouped_fp8_gemm_silu_mul_contiguous.restype = ctypes.c_int
+    lib.grouped_fp8_gemm_silu_mul_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
+    lib.grouped_fp8_gemm_silu_mul_masked.restype = ctypes.c_int
     lib.fp8_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp]
     lib.fp8_quantize_act_1x128.restype = ctypes.c_int
     lib.fp8_quantize_weight_128x128.argtypes = [vp, i32, i64, i64, vp, vp]
@@ -83,6 +92,16 @@ def raw_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out_dt
 def raw_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, stream=0) -> int:
     return load_library().grouped_fp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d,
                                                   G, M_max, N, K, out_dtype, stream)
+
+
+def raw_silu_mul_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, I, K, G, out_dtype, stream=0) -> int:
+    return load_library().grouped_fp8_gemm_silu_mul_contiguous(a, a_scale, b, b_scale, grouped_layout, d,
+                                                               M, I, K, G, out_dtype, stream)
+
+
+def raw_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, I, K, out_dtype, stream=0) -> int:
+    return load_library().grouped_fp8_gemm_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d,
+                                                           G, M_max, I, K, out_dtype, stream)
 
 
 def raw_quantize_act_device(x, in_dtype, G, M, K, q, scale_t, stream=0) -> int:
@@ -170,6 +189,52 @@ def grouped_fp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d, stream=None):
         _dev_ptr(masked_m, "masked_m", (torch.int32,), dev),
         _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev),
         G, Mmax, N, K, _out_code(d), _stream_handle(stream, dev)))
+    return d
+
+
+def grouped_fp8_gemm_silu_mul_contiguous(a, a_scale, b, b_scale, grouped_layout, d, stream=None):
+    """gemm1 + silu_mul, contiguous layout: for rows of expert g, ``h = A[row] . B[g]^T``
+    and ``d[row] = silu(h[:I]) * h[I:]`` (asynchronous on ``stream``).
+
+    b [G, 2I, K] e4m3 (gate rows then up rows), b_scale [G, 2I/128, ceil(K/128)],
+    d [M, I] bfloat16/float16; a, a_scale, grouped_layout as for the GEMM.
+    """
+    torch = _torch()
+    dev = d.device
+    f8 = (torch.uint8, torch.float8_e4m3fn)
+    M, K = a.shape
+    G, N2, Kb = b.shape
+    if N2 % 2 or Kb != K or tuple(d.shape) != (M, N2 // 2) or tuple(grouped_layout.shape) != (M,):
+        raise ValueError("shape mismatch between a, b [G, 2I, K], grouped_layout and d [M, I]")
+    if tuple(a_scale.shape) != (-(-K // 128), M) or tuple(b_scale.shape) != (G, -(-N2 // 128), -(-K // 128)):
+        raise ValueError("scale tensor shapes do not match the (1,128)/(128,128) layouts")
+    _check(raw_silu_mul_contiguous(
+        _dev_ptr(a, "a", f8, dev), _dev_ptr(a_scale, "a_scale", (torch.uint8,), dev),
+        _dev_ptr(b, "b", f8, dev), _dev_ptr(b_scale, "b_scale", (torch.uint8,), dev),
+        _dev_ptr(grouped_layout, "grouped_layout", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev),
+        M, N2 // 2, K, G, _out_code(d), _stream_handle(stream, dev)))
+    return d
+
+
+def grouped_fp8_gemm_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d, stream=None):
+    """gemm1 + silu_mul, masked layout: rows m < masked_m[g] of group g get
+    ``silu(h[:I]) * h[I:]`` with ``h = A[g, m] . B[g]^T``; d [G, M_max, I]."""
+    torch = _torch()
+    dev = d.device
+    f8 = (torch.uint8, torch.float8_e4m3fn)
+    G, Mmax, K = a.shape
+    Gb, N2, Kb = b.shape
+    if N2 % 2 or Gb != G or Kb != K or tuple(d.shape) != (G, Mmax, N2 // 2) or tuple(masked_m.shape) != (G,):
+        raise ValueError("shape mismatch between a, b [G, 2I, K], masked_m and d [G, M_max, I]")
+    if tuple(a_scale.shape) != (G, -(-K // 128), Mmax) or tuple(b_scale.shape) != (G, -(-N2 // 128), -(-K // 128)):
+        raise ValueError("scale tensor shapes do not match the (1,128)/(128,128) layouts")
+    _check(raw_silu_mul_masked(
+        _dev_ptr(a, "a", f8, dev), _dev_ptr(a_scale, "a_scale", (torch.uint8,), dev),
+        _dev_ptr(b, "b", f8, dev), _dev_ptr(b_scale, "b_scale", (torch.uint8,), dev),
+        _dev_ptr(masked_m, "masked_m", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev),
+        G, Mmax, N2 // 2, K, _out_code(d), _stream_handle(stream, dev)))
     return d
 
 

@@ -135,10 +135,13 @@ __device__ __forceinline__ int scale_byte(int word, const uint8_t* row, int kb) 
 // Per-tile, per-lane constants of the K loop.  SAW: the lane's four A-scale
 // bytes (rows 4*l16 .. 4*l16+3 of its wave's 64) are read as one aligned dword
 // (scale rows a multiple of 4 bytes apart); otherwise as four bytes.
-template <int BN_, bool SAW_>
+template <int BN_, bool SAW_, bool SILU_ = false>
 struct TileCtx {
     static constexpr int BN = BN_;
     static constexpr bool SAW = SAW_;
+    // gemm1 with silu_mul: the B tile holds gate and up rows, and fragments
+    // x < FN/2 (gate) take the gate block's scale, x >= FN/2 (up) the up block's
+    static constexpr bool SILU = SILU_;
     static constexpr int WAVES = NTHREADS / 64;
     static constexpr int WN = BN / 4;               // columns per wave (2 x 4 wave grid)
     static constexpr int FN = WN / 16;              // 16-column MFMA tiles per wave
@@ -157,6 +160,7 @@ struct TileCtx {
     const uint8_t* b_tile;            // B row n0 of expert g, K 0
     __amdgpu_buffer_rsrc_t sa_rsrc;   // scale_a from row m0 of K-block 0 to the region's end
     const uint8_t* sb_row;            // scale_b row (all K-blocks) of this wave's 128-column block
+    const uint8_t* sbu_row;           // SILU: scale_b row of the up block (sb_row: the gate block)
     uint32_t sa_stride;        // scale_a bytes between K-blocks (rows of the region)
     uint32_t a_off[A_DMA];     // per-lane source offsets of this wave's DMA chunks
     uint32_t b_off[B_DMA];
@@ -196,9 +200,10 @@ __device__ __forceinline__ int sa_word(const int (&sa)[4]) {
 // out with swz_a(), B with swz()) and this lane's scales into (sa, sb).
 template <class C>
 __device__ __forceinline__ void issue_stage(const C& c, GFG_LDS uint8_t* __restrict__ dst,
-                                            int kb, int wave, int (&sa)[4], int& sb) {
+                                            int kb, int wave, int (&sa)[4], int& sb, int& sbu) {
     load_sa(c, kb, sa);
     sb = load_scale_word(c.sb_row, kb);
+    if constexpr (C::SILU) sbu = load_scale_word(c.sbu_row, kb);
     // K-block base pointers made opaque scalars, so each DMA address is a scalar
     // base plus this lane's 32-bit offset (no per-lane 64-bit induction variables)
     const uint8_t* ak = uniform_ptr(c.a_tile + int64_t(kb) * BK);
@@ -236,20 +241,20 @@ __device__ __forceinline__ void read_frags(const C& c, const GFG_LDS uint8_t* __
 // MFMAs of A fragment Y against every B fragment: the A scale is byte Y of
 // the packed word (op_sel picks it), the B scale the wave's byte.
 template <class C, int Y>
-__device__ __forceinline__ void mfma_row(const Frags<C::BN>& f, int saw, int sb, v4f (&acc)[C::FN][4]) {
+__device__ __forceinline__ void mfma_row(const Frags<C::BN>& f, int saw, int sb, int sbu, v4f (&acc)[C::FN][4]) {
 #pragma unroll
     for (int x = 0; x < C::FN; ++x)
-        acc[x][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[x], f.a[Y], acc[x][Y], 0, 0, 0, sb, Y,
-                                                                     saw);
+        acc[x][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            f.b[x], f.a[Y], acc[x][Y], 0, 0, 0, (C::SILU && x >= C::FN / 2) ? sbu : sb, Y, saw);
 }
 
 template <class C>
-__device__ __forceinline__ void mfma_stage(const Frags<C::BN>& f, int saw, int sb, v4f (&acc)[C::FN][4]) {
+__device__ __forceinline__ void mfma_stage(const Frags<C::BN>& f, int saw, int sb, int sbu, v4f (&acc)[C::FN][4]) {
     static_assert(C::FM == 4, "four A fragments per wave");
-    mfma_row<C, 0>(f, saw, sb, acc);
-    mfma_row<C, 1>(f, saw, sb, acc);
-    mfma_row<C, 2>(f, saw, sb, acc);
-    mfma_row<C, 3>(f, saw, sb, acc);
+    mfma_row<C, 0>(f, saw, sb, sbu, acc);
+    mfma_row<C, 1>(f, saw, sb, sbu, acc);
+    mfma_row<C, 2>(f, saw, sb, sbu, acc);
+    mfma_row<C, 3>(f, saw, sb, sbu, acc);
 }
 
 // One K-step k.  On entry: fragments of stage k are in `cur` (their LDS reads
@@ -278,7 +283,7 @@ template <class C, bool ISSUE, bool READ, int VMWAIT>
 __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__ refill,
                                        const GFG_LDS uint8_t* __restrict__ next, int kb_cur, int kb_refill,
                                        int wave,
-                                       Frags<C::BN>& cur, Frags<C::BN>& nxt, int (&sa)[4], int& sb,
+                                       Frags<C::BN>& cur, Frags<C::BN>& nxt, int (&sa)[4], int& sb, int& sbu,
                                        v4f (&acc)[C::FN][4]) {
     __builtin_amdgcn_sched_barrier(0);
     GFG_WAITCNT(VMWAIT, 0);
@@ -287,6 +292,7 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
     __builtin_amdgcn_sched_barrier(0);
     const int sa_use = sa_word<C>(sa);
     const int sb_use = scale_byte(sb, c.sb_row, kb_cur);
+    const int sbu_use = C::SILU ? scale_byte(sbu, c.sbu_row, kb_cur) : sb_use;
     // The LDS DMA and the fragment reads are issued here, through this
     // function's restrict parameters, so the compiler knows the refilled
     // buffer and the buffer being read do not overlap and adds no wait for
@@ -318,10 +324,11 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
             nxt.b[x] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     }
-    mfma_stage<C>(cur, sa_use, sb_use, acc);
+    mfma_stage<C>(cur, sa_use, sb_use, sbu_use, acc);
     if (ISSUE) {   // after the MFMAs that read the old scale registers
         load_sa(c, kb_refill, sa);
         sb = load_scale_word(c.sb_row, kb_refill);
+        if constexpr (C::SILU) sbu = load_scale_word(c.sbu_row, kb_refill);
     }
     sched_pattern<0, C::FN * C::FM, ISSUE ? C::A_DMA + C::B_DMA : 0, READ ? 2 * (C::FM + C::FN) : 0,
                   ISSUE ? C::SA_LOADS : 0>();
@@ -329,9 +336,30 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BN, bool MASKED, bool SAW, typename OutT>
+// silu(g) * u on four fp32 values: silu(g) = g / (1 + e^-g), the exponential
+// by the hardware base-2 exponential (e^-g = 2^(-g * log2 e)) and the division
+// by the hardware reciprocal.  Large negative g gives 1 + e^-g = inf and
+// silu = -0; large positive g gives e^-g = 0 and silu = g.
+__device__ __forceinline__ v4f silu_mul4(v4f gv, v4f uv) {
+    v4f r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(gv[i] * -1.44269504088896341f);
+        r[i] = gv[i] * __builtin_amdgcn_rcpf(1.0f + e) * uv[i];
+    }
+    return r;
+}
+
+// SILU (gemm1 of the expert MLP): B[g] holds 2*I rows, gate rows [0, I) and
+// up rows [I, 2*I); the output is [rows][I] = silu(gate) * up.  A tile covers
+// 128 output columns o0.. and stages the 128 matching gate rows and 128 up rows
+// as its 256 B rows, interleaved so that each wave's 64 columns are 32 gate
+// and the same 32 up columns: fragments x and x + FN/2 of a lane then hold the
+// gate and up values of the same four outputs.
+template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p) {
-    using C = TileCtx<BN, SAW>;
+    static_assert(!SILU || BN == 256, "the gate/up interleave assumes 64 B rows per wave");
+    using C = TileCtx<BN, SAW, SILU>;
     constexpr int FN = C::FN, FM = C::FM, WN = C::WN;
     constexpr int L = C::LOADS;
 
@@ -389,6 +417,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
 
     const int KB = p.K / BK;
     const int NB = p.N / 128;
+    const int n_out = SILU ? p.N / 2 : p.N;   // output row length
     const int wm = wave & 1, wn = wave >> 1;
     const int l16 = lane & 15, lq = lane >> 4;
     GFG_LDS uint8_t* const buf0 = (GFG_LDS uint8_t*)smem0;
@@ -420,7 +449,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             m0 = int64_t(cand - g * p.mt_per_group) * BM;
             a_reg = p.a + int64_t(g) * p.rows * p.K;
             sa_reg = p.a_scale + int64_t(g) * KB * p.rows;
-            d_reg = reinterpret_cast<uint8_t*>(p.d) + int64_t(g) * p.rows * p.N * int64_t(sizeof(OutT));
+            d_reg = reinterpret_cast<uint8_t*>(p.d) + int64_t(g) * p.rows * n_out * int64_t(sizeof(OutT));
             mlimit = int(m0) + aux;
         } else {
             m0 = int64_t(cand) * BM;
@@ -430,13 +459,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             d_reg = reinterpret_cast<uint8_t*>(p.d);
             mlimit = int(p.rows);
         }
-        const int n0 = nt * BN;
+        // first B row (GEMM; SILU: first gate row) and first output column
+        const int n0 = nt * (SILU ? BN / 2 : BN);
 
         C c;
         c.a_tile = a_reg + m0 * p.K;
         c.b_tile = p.b + (int64_t(g) * p.N + n0) * p.K;
         c.sa_rsrc = make_rsrc(sa_reg + m0, uint32_t(int64_t(KB) * p.rows - m0));
-        c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB);
+        if constexpr (SILU) {
+            c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + n0 / 128) * KB);
+            c.sbu_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n_out + n0) / 128) * KB);
+        } else {
+            c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB);
+        }
         c.sa_stride = uint32_t(p.rows);
         // DMA chunk j of this wave fills LDS rows 8*(j*WAVES + wave) .. +7; lane i
         // writes physical chunk i%8 of tile row R = +i/8, which holds logical
@@ -452,8 +487,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
                 c.a_off[j] = uint32_t(row - m0) * uint32_t(p.K) + uint32_t(lc * 16);
             }
 #pragma unroll
-            for (int j = 0; j < C::B_DMA; ++j)
-                c.b_off[j] = uint32_t(8 * (j * C::WAVES + wave) + rr) * uint32_t(p.K) + uint32_t((pc ^ rr) * 16);
+            for (int j = 0; j < C::B_DMA; ++j) {
+                const int R = 8 * (j * C::WAVES + wave) + rr;       // LDS row
+                // SILU: LDS rows 64w .. 64w+31 hold gate rows o0 + 32w .., rows
+                // 64w+32 .. 64w+63 the up rows I + o0 + 32w .. (B rows from n0)
+                const int w = R >> 6, q = R & 63;
+                const int brow = !SILU ? R : (q < 32 ? 32 * w + q : n_out + 32 * w + (q - 32));
+                c.b_off[j] = uint32_t(brow) * uint32_t(p.K) + uint32_t((pc ^ rr) * 16);
+            }
         }
         // A-scale offsets (from row m0 of K-block 0): the lane's rows are
         // wm*64 + 4*l16 + f.  The dword form needs no clamp: rows come in
@@ -489,7 +530,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             for (int y = 0; y < FM; ++y) acc[x][y] = v4f{0.f, 0.f, 0.f, 0.f};
 
         Frags<BN> fa, fb;
-        int sa0[4], sa1[4], sa2[4], sb0 = 0, sb1 = 0, sb2 = 0;
+        int sa0[4], sa1[4], sa2[4], sb0 = 0, sb1 = 0, sb2 = 0, su0 = 0, su1 = 0, su2 = 0;
 
         // Contiguous layout: the expert of each of this lane's four output rows
         // (4*l16 + y, consecutive grouped_layout entries), read now so that the
@@ -505,9 +546,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
 
         // prologue: stages 0..2 in flight (clamped to the last stage), stage 0's
         // fragments in `fa`
-        issue_stage(c, buf0, 0, wave, sa0, sb0);
-        issue_stage(c, buf1, min(1, KB - 1), wave, sa1, sb1);
-        issue_stage(c, buf2, min(2, KB - 1), wave, sa2, sb2);
+        issue_stage(c, buf0, 0, wave, sa0, sb0, su0);
+        issue_stage(c, buf1, min(1, KB - 1), wave, sa1, sb1, su1);
+        issue_stage(c, buf2, min(2, KB - 1), wave, sa2, sb2, su2);
         GFG_WAITCNT(2 * L, 15);
         __builtin_amdgcn_s_barrier();
         read_frags(c, buf0, fa);
@@ -517,27 +558,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         // reads any more) and reads stage k+1's fragments (past the end: unused).
         int kb = 0;
         for (; kb + 3 <= KB; kb += 3) {
-            k_step<C, true, true, L>(c, buf0, buf1, kb, min(kb + 3, KB - 1), wave, fa, fb, sa0, sb0, acc);
-            k_step<C, true, true, L>(c, buf1, buf2, kb + 1, min(kb + 4, KB - 1), wave, fa, fb, sa1, sb1, acc);
-            k_step<C, true, true, L>(c, buf2, buf0, kb + 2, min(kb + 5, KB - 1), wave, fa, fb, sa2, sb2, acc);
+            k_step<C, true, true, L>(c, buf0, buf1, kb, min(kb + 3, KB - 1), wave, fa, fb, sa0, sb0, su0, acc);
+            k_step<C, true, true, L>(c, buf1, buf2, kb + 1, min(kb + 4, KB - 1), wave, fa, fb, sa1, sb1, su1, acc);
+            k_step<C, true, true, L>(c, buf2, buf0, kb + 2, min(kb + 5, KB - 1), wave, fa, fb, sa2, sb2, su2, acc);
         }
-        if (KB - kb >= 1) k_step<C, true, true, L>(c, buf0, buf1, kb, KB - 1, wave, fa, fb, sa0, sb0, acc);
-        if (KB - kb >= 2) k_step<C, true, true, L>(c, buf1, buf2, kb + 1, KB - 1, wave, fa, fb, sa1, sb1, acc);
+        if (KB - kb >= 1) k_step<C, true, true, L>(c, buf0, buf1, kb, KB - 1, wave, fa, fb, sa0, sb0, su0, acc);
+        if (KB - kb >= 2) k_step<C, true, true, L>(c, buf1, buf2, kb + 1, KB - 1, wave, fa, fb, sa1, sb1, su1, acc);
         // every wave is done with LDS before the next tile's prologue refills it
         GFG_WAITCNT(0, 0);
         __builtin_amdgcn_s_barrier();
 
         // ---- epilogue: lane owns row (4*l16 + y), columns 16x + 4lq .. +3 ----
+        // (SILU: output columns o0 + 32*wn + 16x + 4lq .. +3 for x < FN/2, from
+        // gate fragment x and up fragment x + FN/2)
+        typedef OutT out4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int y = 0; y < FM; ++y) {
             const int row = int(m0) + wm * 64 + 4 * l16 + y;   // rows of a region fit in 32 bits
             const bool ok = row < mlimit && (MASKED || int(lay[y]) == g);
             if (!ok) continue;
-            OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * p.N + n0 + wn * WN + 4 * lq;
+            if constexpr (SILU) {
+                OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * n_out + n0 + wn * (WN / 2) + 4 * lq;
 #pragma unroll
-            for (int x = 0; x < FN; ++x) {
-                typedef OutT out4 __attribute__((ext_vector_type(4)));
-                *reinterpret_cast<out4*>(drow + x * 16) = __builtin_convertvector(acc[x][y], out4);
+                for (int x = 0; x < FN / 2; ++x)
+                    *reinterpret_cast<out4*>(drow + x * 16) =
+                        __builtin_convertvector(silu_mul4(acc[x][y], acc[x + FN / 2][y]), out4);
+            } else {
+                OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * p.N + n0 + wn * WN + 4 * lq;
+#pragma unroll
+                for (int x = 0; x < FN; ++x)
+                    *reinterpret_cast<out4*>(drow + x * 16) = __builtin_convertvector(acc[x][y], out4);
             }
         }
     }
@@ -567,7 +617,7 @@ int device_info(DeviceInfo* out) {
     return GFG_OK;
 }
 
-template <int BN, bool MASKED, bool SAW, typename OutT>
+template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU = false>
 int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     DeviceInfo di;
     if (int rc = device_info(&di)) return rc;
@@ -576,7 +626,7 @@ int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     unsigned grid = upper < unsigned(di.cus) ? upper : unsigned(di.cus);
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;          // whole slots on every XCD
     if (grid == 0) return GFG_OK;
-    hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, SAW, OutT>), dim3(grid), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, SAW, OutT, SILU>), dim3(grid), dim3(NTHREADS), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(GFG_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GFG_OK;
@@ -620,6 +670,76 @@ int check_common(const char* fn, const void* a, const void* sa, const void* b, c
 
 int group_m_default() { return 4; }
 
+// Parameters of a contiguous call: M rows of A mapped to experts by
+// grouped_layout, B [G][N][K].  Returns GFG_OK with *n_cand set, or an error.
+int contig_params(const char* fn, const void* a, const uint8_t* a_scale, const void* b, const uint8_t* b_scale,
+                  const int32_t* grouped_layout, void* d, int64_t M, int64_t N, int64_t K, int32_t G,
+                  int32_t out_dtype, Params* p, int64_t* n_cand) {
+    if (M < 0) return fail(GFG_EINVAL, "%s: M=%lld is negative", fn, (long long)M);
+    if (int rc = check_common(fn, a, a_scale, b, b_scale, grouped_layout, d, N, K, G, out_dtype)) return rc;
+    *n_cand = (M + BM - 1) / BM;
+    if (*n_cand > MT_MAX)
+        return fail(GFG_EUNSUPPORTED, "%s: M=%lld exceeds %d rows", fn, (long long)M, MT_MAX * BM);
+    *p = Params{};
+    p->a = static_cast<const uint8_t*>(a);
+    p->a_scale = a_scale;
+    p->b = static_cast<const uint8_t*>(b);
+    p->b_scale = b_scale;
+    p->meta = grouped_layout;
+    p->d = d;
+    p->rows = M;
+    p->N = int(N);
+    p->K = int(K);
+    p->G = G;
+    p->n_cand = int(*n_cand);
+    p->mt_per_group = 0;
+    p->group_m = group_m_default();
+    return GFG_OK;
+}
+
+// Parameters of a masked call: A [G][M_max][K], rows m < masked_m[g] computed.
+int masked_params(const char* fn, const void* a, const uint8_t* a_scale, const void* b, const uint8_t* b_scale,
+                  const int32_t* masked_m, void* d, int32_t G, int64_t M_max, int64_t N, int64_t K,
+                  int32_t out_dtype, Params* p, int64_t* n_cand) {
+    if (M_max < 0) return fail(GFG_EINVAL, "%s: M_max=%lld is negative", fn, (long long)M_max);
+    if (int rc = check_common(fn, a, a_scale, b, b_scale, masked_m, d, N, K, G, out_dtype)) return rc;
+    const int64_t per = (M_max + BM - 1) / BM;
+    *n_cand = per * G;
+    if (*n_cand > MT_MAX)
+        return fail(GFG_EUNSUPPORTED, "%s: G*ceil(M_max/128)=%lld exceeds %d", fn, (long long)*n_cand, MT_MAX);
+    *p = Params{};
+    p->a = static_cast<const uint8_t*>(a);
+    p->a_scale = a_scale;
+    p->b = static_cast<const uint8_t*>(b);
+    p->b_scale = b_scale;
+    p->meta = masked_m;
+    p->d = d;
+    p->rows = M_max;
+    p->N = int(N);
+    p->K = int(K);
+    p->G = G;
+    p->n_cand = int(*n_cand);
+    p->mt_per_group = int(per);
+    p->group_m = group_m_default();
+    return GFG_OK;
+}
+
+// gemm1 + silu_mul runs on the 256-row B tile with the packed A-scale words.
+int check_silu(const char* fn, int64_t I, int64_t rows, const uint8_t* a_scale) {
+    if (I <= 0) return fail(GFG_EINVAL, "%s: I=%lld must be positive", fn, (long long)I);
+    if (I % 128) return fail(GFG_EUNSUPPORTED, "%s: I=%lld must be a multiple of 128", fn, (long long)I);
+    if (rows % 4 || reinterpret_cast<uintptr_t>(a_scale) % 4)
+        return fail(GFG_EUNSUPPORTED, "%s: needs scale_a rows (%lld) a multiple of 4 and scale_a 4-byte aligned", fn,
+                    (long long)rows);
+    return GFG_OK;
+}
+
+template <bool MASKED>
+int dispatch_silu(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
+    return out_dtype == GFG_OUT_BF16 ? launch_t<256, MASKED, true, __bf16, true>(p, n_cand, s)
+                                     : launch_t<256, MASKED, true, _Float16, true>(p, n_cand, s);
+}
+
 }  // namespace
 }  // namespace gfg
 
@@ -630,27 +750,12 @@ extern "C" int grouped_fp8_gemm_contiguous(const void* a, const uint8_t* a_scale
                                            int64_t M, int64_t N, int64_t K, int32_t G, int32_t out_dtype,
                                            void* stream) {
     clear_error();
-    const char* fn = "grouped_fp8_gemm_contiguous";
-    if (M < 0) return fail(GFG_EINVAL, "%s: M=%lld is negative", fn, (long long)M);
-    if (int rc = check_common(fn, a, a_scale, b, b_scale, grouped_layout, d, N, K, G, out_dtype)) return rc;
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = contig_params("grouped_fp8_gemm_contiguous", a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G,
+                               out_dtype, &p, &n_cand))
+        return rc;
     if (M == 0) return GFG_OK;
-    const int64_t n_cand = (M + BM - 1) / BM;
-    if (n_cand > MT_MAX)
-        return fail(GFG_EUNSUPPORTED, "%s: M=%lld exceeds %d rows", fn, (long long)M, MT_MAX * BM);
-    Params p{};
-    p.a = static_cast<const uint8_t*>(a);
-    p.a_scale = a_scale;
-    p.b = static_cast<const uint8_t*>(b);
-    p.b_scale = b_scale;
-    p.meta = grouped_layout;
-    p.d = d;
-    p.rows = M;
-    p.N = int(N);
-    p.K = int(K);
-    p.G = G;
-    p.n_cand = int(n_cand);
-    p.mt_per_group = 0;
-    p.group_m = group_m_default();
     return dispatch<false>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
 }
 
@@ -658,27 +763,41 @@ extern "C" int grouped_fp8_gemm_masked(const void* a, const uint8_t* a_scale, co
                                        const uint8_t* b_scale, const int32_t* masked_m, void* d, int32_t G,
                                        int64_t M_max, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
     clear_error();
-    const char* fn = "grouped_fp8_gemm_masked";
-    if (M_max < 0) return fail(GFG_EINVAL, "%s: M_max=%lld is negative", fn, (long long)M_max);
-    if (int rc = check_common(fn, a, a_scale, b, b_scale, masked_m, d, N, K, G, out_dtype)) return rc;
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = masked_params("grouped_fp8_gemm_masked", a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K,
+                               out_dtype, &p, &n_cand))
+        return rc;
     if (M_max == 0) return GFG_OK;
-    const int64_t per = (M_max + BM - 1) / BM;
-    const int64_t n_cand = per * G;
-    if (n_cand > MT_MAX)
-        return fail(GFG_EUNSUPPORTED, "%s: G*ceil(M_max/128)=%lld exceeds %d", fn, (long long)n_cand, MT_MAX);
-    Params p{};
-    p.a = static_cast<const uint8_t*>(a);
-    p.a_scale = a_scale;
-    p.b = static_cast<const uint8_t*>(b);
-    p.b_scale = b_scale;
-    p.meta = masked_m;
-    p.d = d;
-    p.rows = M_max;
-    p.N = int(N);
-    p.K = int(K);
-    p.G = G;
-    p.n_cand = int(n_cand);
-    p.mt_per_group = int(per);
-    p.group_m = group_m_default();
     return dispatch<true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int grouped_fp8_gemm_silu_mul_contiguous(const void* a, const uint8_t* a_scale, const void* b,
+                                                    const uint8_t* b_scale, const int32_t* grouped_layout, void* d,
+                                                    int64_t M, int64_t I, int64_t K, int32_t G, int32_t out_dtype,
+                                                    void* stream) {
+    clear_error();
+    const char* fn = "grouped_fp8_gemm_silu_mul_contiguous";
+    if (int rc = check_silu(fn, I, M < 0 ? 0 : M, a_scale)) return rc;
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, 2 * I, K, G, out_dtype, &p, &n_cand))
+        return rc;
+    if (M == 0) return GFG_OK;
+    return dispatch_silu<false>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int grouped_fp8_gemm_silu_mul_masked(const void* a, const uint8_t* a_scale, const void* b,
+                                                const uint8_t* b_scale, const int32_t* masked_m, void* d, int32_t G,
+                                                int64_t M_max, int64_t I, int64_t K, int32_t out_dtype,
+                                                void* stream) {
+    clear_error();
+    const char* fn = "grouped_fp8_gemm_silu_mul_masked";
+    if (int rc = check_silu(fn, I, M_max < 0 ? 0 : M_max, a_scale)) return rc;
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, 2 * I, K, out_dtype, &p, &n_cand))
+        return rc;
+    if (M_max == 0) return GFG_OK;
+    return dispatch_silu<true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
 }

@@ -16,6 +16,16 @@ Recipe (numpy PCG64, seed = 1000 + workload index):
   * random group sizes are integers uniform on [100, 1024] inclusive;
   * random masked_m are integers uniform on [0, 1024] inclusive, then two
     seeded distinct groups are set to 0 and 1024.
+
+gemm1 with silu_mul (third reference page, the MoE gemm1/gemm2 pull request,
+section "Results"): the Kimi-K2.5 TP=4 expert shape, 385 experts, hidden size
+K = 7168, intermediate size I = 512 (so B[g] is [2*I, K]: gate rows, then up
+rows), top-9 routing.  For a batch of T tokens each token picks 9 distinct
+experts uniformly at random (seeded), and an expert's rows are the tokens
+routed to it, padded to a multiple of 128.  The 385 weight matrices are 8
+seeded N(0,1) draws repeated in turn (expert g uses draw g % 8): the kernel
+reads 385 separate copies from device memory, but the host draws and
+quantizes only 8 (11 GB of float32 otherwise).
 """
 from __future__ import annotations
 
@@ -39,6 +49,13 @@ class Workload:
     M_max: int = 0                                    # masked: rows per group buffer
     masked_m: list = field(default_factory=list)      # masked: valid rows per group
     row_log10_range: tuple | None = None              # per-token magnitude 10**U(lo, hi)
+    op: str = "gemm"                                  # "gemm" or "silu_mul" (N = 2*I)
+    b_distinct: int = 0                               # > 0: expert g's B is draw g % b_distinct
+
+    @property
+    def I(self) -> int:
+        """silu_mul output width (half of B's rows)."""
+        return self.N // 2
 
     @property
     def M(self) -> int:
@@ -96,6 +113,21 @@ def context_workloads() -> list[Workload]:
                      m_per_group=[4096])]
 
 
+def _topk_counts(rng: np.random.Generator, tokens: int, experts: int, k: int) -> list:
+    """Rows per expert when each of `tokens` tokens picks k distinct experts uniformly."""
+    counts = np.zeros(experts, dtype=np.int64)
+    for _ in range(tokens):
+        counts[rng.choice(experts, size=k, replace=False)] += 1
+    return [int(c) for c in counts]
+
+
+def gemm1_workloads() -> list[Workload]:
+    """gemm1 + silu_mul at the Kimi-K2.5 TP=4 expert shape (385 experts,
+    K = 7168, I = 512, top 9) for a 4096-token batch, seed 1006."""
+    return [Workload("kimi_tp4_gemm1_t4096", "contiguous", 385, 1024, 7168, "bf16", 1006,
+                     m_per_group=_topk_counts(_rng(1006), 4096, 385, 9), op="silu_mul", b_distinct=8)]
+
+
 def workload(name_or_index) -> Workload:
     """A standard workload by index or name, a context workload by name, or an
     ad-hoc one named ``contig_g{G}_m{rows per group}_n{N}_k{K}`` or
@@ -106,6 +138,10 @@ def workload(name_or_index) -> Workload:
     for w in ws + context_workloads():
         if w.name == name_or_index:
             return w
+    if name_or_index.startswith("kimi_"):
+        for w in gemm1_workloads():
+            if w.name == name_or_index:
+                return w
     import re
     m = re.fullmatch(r"(contig|masked)_g(\d+)_m(\d+)_n(\d+)_k(\d+)", name_or_index)
     if m:
@@ -133,6 +169,8 @@ def draw(w: Workload, seed_offset: int = 0):
 
     Contiguous: returns dict(a [M, K], b [G, N, K], grouped_layout [M]).
     Masked:     returns dict(a [G, M_max, K], b [G, N, K], masked_m [G]).
+    With ``b_distinct`` > 0, ``b`` holds only the distinct draws
+    [b_distinct, N, K] and ``b_index`` [G] names the draw each expert uses.
     ``seed_offset`` gives independent input sets of the same shape.
     """
     rng = _rng(w.seed + 7919 * seed_offset)
@@ -148,7 +186,11 @@ def draw(w: Workload, seed_offset: int = 0):
         lo, hi = w.row_log10_range
         mag = np.power(10.0, rng.uniform(lo, hi, size=a.shape[:-1] + (1,))).astype(np.float32)
         a *= mag
-    out["b"] = rng.standard_normal((w.G, w.N, w.K), dtype=np.float32)
+    if w.b_distinct:
+        out["b"] = rng.standard_normal((w.b_distinct, w.N, w.K), dtype=np.float32)
+        out["b_index"] = np.arange(w.G, dtype=np.int64) % w.b_distinct
+    else:
+        out["b"] = rng.standard_normal((w.G, w.N, w.K), dtype=np.float32)
     return out
 
 

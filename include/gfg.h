@@ -105,6 +105,40 @@ GFG_API int grouped_fp8_gemm_masked(const void* a, const uint8_t* a_scale,
                             int32_t out_dtype, void* stream);
 
 /*
+ * gemm1 of the expert MLP with its silu_mul epilogue (third reference page,
+ * the pull request "flydsl mxfp4 a4w4 MoE: bring gemm1/gemm2 to parity with
+ * the HIP backend", section "Changes", item gemm1), on the FP8 block-scaled
+ * operands above.  Each expert's B holds 2*I rows: rows [0, I) are the gate
+ * projection, rows [I, 2*I) the up projection.  For every computed row m:
+ *
+ *   h = A[m] . B[g]^T  (length 2*I, fp32),   out[m, j] = silu(h[j]) * h[I + j]
+ *
+ * with silu(x) = x / (1 + e^-x), e^-x taken by the hardware base-2
+ * exponential and the division by the hardware reciprocal, then one rounding
+ * to bf16 or f16.  Rows are chosen exactly as in the GEMMs above.
+ *
+ *   b        [G][2*I][K]                     e4m3 bytes (gate rows, then up rows)
+ *   b_scale  [G][2*I/128][ceil(K/128)]       E8M0 bytes
+ *   d        contiguous [M][I], masked [G][M_max][I]   bf16 or f16
+ *   (a, a_scale, grouped_layout, masked_m as in the GEMMs)
+ *
+ * Sizes: as the GEMM with N = 2*I, and I a positive multiple of 128
+ * (else GFG_EUNSUPPORTED; I <= 0 is GFG_EINVAL).  These entry points also
+ * need M (M_max) a multiple of 4 and a_scale 4-byte aligned
+ * (else GFG_EUNSUPPORTED).
+ */
+GFG_API int grouped_fp8_gemm_silu_mul_contiguous(const void* a, const uint8_t* a_scale,
+                                         const void* b, const uint8_t* b_scale,
+                                         const int32_t* grouped_layout, void* d,
+                                         int64_t M, int64_t I, int64_t K, int32_t G,
+                                         int32_t out_dtype, void* stream);
+GFG_API int grouped_fp8_gemm_silu_mul_masked(const void* a, const uint8_t* a_scale,
+                                     const void* b, const uint8_t* b_scale,
+                                     const int32_t* masked_m, void* d,
+                                     int32_t G, int64_t M_max, int64_t I, int64_t K,
+                                     int32_t out_dtype, void* stream);
+
+/*
  * Host quantizers (CPU, synchronous), ceil-E8M0 scales and nearest-even E4M3:
  * for each block, t = the smallest integer with 448 * 2^t >= amax (t = 0 for
  * an all-zero block), scale byte = t + 127, q = E4M3(x / 2^t).  The rounding

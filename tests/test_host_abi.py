@@ -167,3 +167,41 @@ def test_gemm_empty_and_oversize():
     assert _m(Mmax=-5) == 1
     assert _c(M=4096 * 128 + 1) == 2
     assert _m(G=33, Mmax=128 * 128) == 2
+
+
+def _sc(**kw):
+    args = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, meta=FAKE, d=FAKE, M=256, I=256, K=256, G=2, dt=0)
+    args.update(kw)
+    return gfg.raw_silu_mul_contiguous(args["a"], args["sa"], args["b"], args["sb"], args["meta"], args["d"],
+                                       args["M"], args["I"], args["K"], args["G"], args["dt"], 0)
+
+
+def _sm(**kw):
+    args = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, meta=FAKE, d=FAKE, G=2, Mmax=256, I=256, K=256, dt=0)
+    args.update(kw)
+    return gfg.raw_silu_mul_masked(args["a"], args["sa"], args["b"], args["sb"], args["meta"], args["d"],
+                                   args["G"], args["Mmax"], args["I"], args["K"], args["dt"], 0)
+
+
+@pytest.mark.parametrize("fn", [_sc, _sm])
+def test_silu_mul_argument_errors(fn):
+    for k in ("a", "sa", "b", "sb", "meta", "d"):
+        assert fn(**{k: None}) == 1, k
+    assert fn(dt=2) == 1
+    assert fn(G=0) == 1
+    assert fn(I=0) == 1
+    assert fn(I=-128) == 1
+    assert fn(K=300) == 2
+    assert fn(I=192) == 2          # I must be a multiple of 128 (the output tile)
+    assert "multiple of 128" in gfg.load_library().gfg_last_error().decode()
+    assert fn(sa=FAKE + 2) == 2    # the packed A-scale words need 4-byte alignment
+    rows = {"M": 258} if fn is _sc else {"Mmax": 258}
+    assert fn(**rows) == 2         # scale rows not a multiple of 4
+    assert "multiple of 4" in gfg.load_library().gfg_last_error().decode()
+
+
+def test_silu_mul_empty_is_noop():
+    assert _sc(M=0) == 0
+    assert _sm(Mmax=0) == 0
+    assert _sc(M=-4) == 1
+    assert _sm(Mmax=-4) == 1
