@@ -287,6 +287,94 @@ def grouped_gemm_silu_mul_masked(q_a, scale_a, q_b, scale_b, masked_m, out_init=
     return out
 
 
+# ---------------------------------------------------------------- MXFP8 (1 x 32 blocks)
+# The MX variant (third reference page: the MoE kernels there are "mxfp4
+# (a4w4)" with E8M0 scales under the rounding it calls "Even"; section
+# "Notes").  MX formats share one E8M0 scale per 32 consecutive elements along
+# K, for activations and weights alike.  Readings of what the page leaves
+# open, for the FP8 (E4M3) element type:
+#   * the scale exponent is floor(log2(amax)) - 8, where 8 is the exponent of
+#     E4M3's largest power of two (256): the scaled block's largest magnitude
+#     lies in [256, 512);
+#   * elements are x / 2**t rounded to nearest, ties to even ("Even"), and
+#     clamped to +-448 (scaled values in (448, 512) saturate);
+#   * an all-zero block gets t = 0 (byte 127); t outside [-127, 127] is an error;
+#   * both scale tensors are stored transposed, one row of bytes per 32-wide
+#     K block: ``[K/32, M]`` for A, ``[G, K/32, N]`` for B.
+
+MX_BLOCK = 32
+MX_EMAX = 8                # E4M3: largest power of two is 2**8
+
+
+def mx_exponent(amax: np.ndarray) -> np.ndarray:
+    """t = floor(log2(amax)) - 8 exactly (frexp), 0 where amax == 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    if np.any(~np.isfinite(amax)) or np.any(amax < 0):
+        raise ValueError("mx_exponent: amax must be finite and >= 0")
+    _, p = np.frexp(np.where(amax > 0, amax, 1.0))     # amax = f * 2**p, f in [0.5, 1)
+    t = np.where(amax > 0, p.astype(np.int64) - 1 - MX_EMAX, 0)
+    if np.any(t < -127) or np.any(t > 127):
+        raise ValueError("mx_exponent: scale outside the E8M0 range")
+    return t
+
+
+def quantize_mx_1x32(x: np.ndarray):
+    """MX quantization of x[..., R, K] along K (K a multiple of 32).
+
+    Returns ``(q [..., R, K] uint8 e4m3, scale_t [..., K/32, R] uint8 e8m0)``
+    with, per row r and 32-wide block j: t = mx_exponent(max |block|),
+    q = RNE_e4m3(clamp(x / 2**t, -448, 448)), byte = t + 127.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    *lead, R, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("quantize_mx_1x32: K must be a multiple of 32")
+    xb = x.reshape(*lead, R, K // MX_BLOCK, MX_BLOCK)
+    t = mx_exponent(np.abs(xb).max(axis=-1))                         # [..., R, K/32]
+    v = np.clip(xb / np.exp2(t[..., None].astype(np.float64)), -FP8_MAX, FP8_MAX)
+    q = encode_e4m3_rne(v).reshape(*lead, R, K)
+    st = np.swapaxes((t + 127).astype(np.uint8), -1, -2)             # [..., K/32, R]
+    return np.ascontiguousarray(q), np.ascontiguousarray(st)
+
+
+def dequantize_mx(q: np.ndarray, scale_t: np.ndarray) -> np.ndarray:
+    """X_dq[..., r, k] = e4m3(q[..., r, k]) * 2**(scale_t[..., k // 32, r] - 127)."""
+    s = np.swapaxes(e8m0_value(scale_t), -1, -2)                     # [..., R, K/32]
+    return decode_e4m3(q) * np.repeat(s, MX_BLOCK, axis=-1)
+
+
+def grouped_gemm_mx_contiguous(q_a, scale_a, q_b, scale_b, grouped_layout, d_init=None):
+    """Contiguous grouped GEMM on MX operands, float64: A [M, K] with scale_a
+    [K/32, M], B [G, N, K] with scale_b [G, K/32, N];
+    ``D[rows with grouped_layout == g] = A_dq[rows] @ B_dq[g]^T``, other rows
+    keep ``d_init``."""
+    a = dequantize_mx(q_a, scale_a)
+    b = dequantize_mx(q_b, scale_b)
+    layout = np.asarray(grouped_layout, dtype=np.int64)
+    M, N = a.shape[0], b.shape[1]
+    d = np.full((M, N), np.nan) if d_init is None else np.array(d_init, dtype=np.float64)
+    for g in range(b.shape[0]):
+        rows = np.nonzero(layout == g)[0]
+        if rows.size:
+            d[rows] = a[rows] @ b[g].T
+    return d
+
+
+def grouped_gemm_mx_masked(q_a, scale_a, q_b, scale_b, masked_m, d_init=None):
+    """Masked grouped GEMM on MX operands: A [G, M_max, K] with scale_a
+    [G, K/32, M_max]; rows m < masked_m[g] computed, others keep ``d_init``."""
+    G, Mmax, K = q_a.shape
+    b = dequantize_mx(q_b, scale_b)
+    N = b.shape[1]
+    d = np.full((G, Mmax, N), np.nan) if d_init is None else np.array(d_init, dtype=np.float64)
+    for g in range(G):
+        mm = int(min(max(int(masked_m[g]), 0), Mmax))
+        if mm:
+            a = dequantize_mx(q_a[g, :mm], scale_a[g][:, :mm])
+            d[g, :mm] = a @ b[g].T
+    return d
+
+
 # ---------------------------------------------------------------- metrics
 def calc_diff(x, y) -> float:
     """1 - 2*sum(x*y) / sum(x*x + y*y), in float64 ("cosine-similarity-style")."""

@@ -553,3 +553,135 @@ def test_silu_mul_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(o, "grouped_gemm_contiguous", real_gc)
     monkeypatch.setattr(o, "grouped_gemm_silu_mul_contiguous", real_sc)
     assert failures == 3
+
+
+# ------------------------------------------------------------------ MXFP8 (1 x 32) pins
+def test_mx_exponent_golden():
+    rows = _read_golden("mx_e8m0_floor.txt")
+    amax = np.array([float(a) for a, _ in rows])
+    want = np.array([int(b) for _, b in rows])
+    assert np.array_equal(o.mx_exponent(amax) + 127, want)
+
+
+def test_mx_exponent_bruteforce():
+    rng = np.random.default_rng(31)
+    amax = np.concatenate([rng.uniform(0, 1, 500) * 10.0 ** rng.uniform(-30, 30, 500),
+                           2.0 ** rng.integers(-100, 100, 50).astype(np.float64),
+                           np.nextafter(2.0 ** rng.integers(-100, 100, 50).astype(np.float64), 0)])
+    t = o.mx_exponent(amax)
+    for a, ti in zip(amax, t):
+        want = next(k for k in range(-140, 140) if 256.0 * 2.0 ** k <= a < 512.0 * 2.0 ** k)
+        assert ti == want, (a, ti, want)
+    with pytest.raises(ValueError):
+        o.mx_exponent(np.array([1e-37]))            # t = -131: below E8M0's range
+
+
+def _bf_quant_mx(x):
+    """Per row, per 32-wide block: brute-force exponent search, clamp, exhaustive RNE encode."""
+    R, K = x.shape
+    q = np.zeros((R, K), np.uint8)
+    s = np.zeros((K // 32, R), np.uint8)
+    for r in range(R):
+        for j in range(K // 32):
+            blk = [float(v) for v in x[r, 32 * j:32 * j + 32]]
+            amax = max(abs(v) for v in blk)
+            t = 0 if amax == 0 else next(k for k in range(-140, 140) if 256.0 * 2.0 ** k <= amax < 512.0 * 2.0 ** k)
+            s[j, r] = t + 127
+            for i, v in enumerate(blk):
+                q[r, 32 * j + i] = _bf_encode(min(max(v / 2.0 ** t, -448.0), 448.0))
+    return q, s
+
+
+def test_mx_quantizer_bruteforce_tiny():
+    """Ragged magnitudes, an all-zero block, and blocks whose scaled maximum
+    lies in (448, 512) (saturating to +-448)."""
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((5, 128)) * 10.0 ** rng.uniform(-3, 3, (5, 1))).astype(np.float32)
+    x[1, 32:64] = 0.0
+    x[2, 64:96] = rng.uniform(-1, 1, 32).astype(np.float32) * 8.0
+    x[2, 70] = 7.75            # t = -6: scaled maximum 7.75 * 64 = 496, saturates to 448
+    x[3, 0:32] = np.float32(500.0)
+    x[3, 5] = np.float32(-470.0)
+    q, s = o.quantize_mx_1x32(x)
+    bq, bs = _bf_quant_mx(x)
+    assert np.array_equal(s, bs)
+    assert np.array_equal(q, bq)
+    assert q[3, 0] == 0x7E and q[3, 5] == 0xFE           # saturated to +-448
+
+
+def _bf_mx_gemm_rows(qa, sa, qb, sb, rows_a, g):
+    """fsum triple loop with per-32 scales on both operands."""
+    N, K = qb.shape[1], qb.shape[2]
+    out = np.zeros((len(rows_a), N))
+    for i, r in enumerate(rows_a):
+        a = [_val(qa[r, k]) * 2.0 ** (int(sa[k // 32, r]) - 127) for k in range(K)]
+        for n in range(N):
+            out[i, n] = math.fsum(a[k] * _val(qb[g, n, k]) * 2.0 ** (int(sb[g, k // 32, n]) - 127)
+                                  for k in range(K))
+    return out
+
+
+def test_mx_contiguous_gemm_bruteforce_tiny():
+    rng = np.random.default_rng(33)
+    layout = np.array([0, -1, 1, 1, 0, -1], np.int32)
+    K, N = 96, 40
+    a = (rng.standard_normal((layout.size, K)) * 10.0 ** rng.uniform(-2, 2, (layout.size, 1))).astype(np.float32)
+    b = rng.standard_normal((2, N, K)).astype(np.float32)
+    qa, sa = o.quantize_mx_1x32(a)
+    qb, sb = o.quantize_mx_1x32(b)
+    assert sa.shape == (K // 32, layout.size) and sb.shape == (2, K // 32, N)
+    d = o.grouped_gemm_mx_contiguous(qa, sa, qb, sb, layout, np.full((layout.size, N), 5.5))
+    for g in range(2):
+        rows = [r for r in range(layout.size) if layout[r] == g]
+        np.testing.assert_allclose(d[rows], _bf_mx_gemm_rows(qa, sa, qb, sb, rows, g), rtol=1e-12, atol=1e-12)
+    assert np.all(d[layout < 0] == 5.5)
+
+
+def test_mx_masked_gemm_bruteforce_tiny():
+    rng = np.random.default_rng(34)
+    G, Mmax, K, N = 2, 4, 64, 24
+    a = rng.standard_normal((G, Mmax, K)).astype(np.float32)
+    b = rng.standard_normal((G, N, K)).astype(np.float32)
+    masked_m = np.array([3, 1], np.int32)
+    qa, sa = o.quantize_mx_1x32(a)
+    qb, sb = o.quantize_mx_1x32(b)
+    assert sa.shape == (G, K // 32, Mmax)
+    d = o.grouped_gemm_mx_masked(qa, sa, qb, sb, masked_m, np.full((G, Mmax, N), -2.0))
+    for g in range(G):
+        mm = int(masked_m[g])
+        np.testing.assert_allclose(d[g, :mm], _bf_mx_gemm_rows(qa[g], sa[g], qb, sb, list(range(mm)), g),
+                                   rtol=1e-12, atol=1e-12)
+        assert np.all(d[g, mm:] == -2.0)
+
+
+def test_mx_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible MX mistakes in the oracle (on the CPU): the ceil rule of
+    the (1,128) path instead of floor, scales applied per 128 instead of per
+    32, and no saturation before encoding."""
+    failures = 0
+    real_exp = o.mx_exponent
+    monkeypatch.setattr(o, "mx_exponent", lambda a: o.e8m0_ceil_exponent(a))
+    try:
+        test_mx_exponent_golden()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "mx_exponent", real_exp)
+    real_dq = o.dequantize_mx
+
+    def per128(q, scale_t):
+        st = np.repeat(np.take(scale_t, np.arange(0, scale_t.shape[-2], 4), axis=-2), 4, axis=-2)
+        return real_dq(q, st[..., :scale_t.shape[-2], :])
+    monkeypatch.setattr(o, "dequantize_mx", per128)
+    try:
+        test_mx_contiguous_gemm_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "dequantize_mx", real_dq)
+    real_clip = np.clip
+    monkeypatch.setattr(o.np, "clip", lambda v, lo, hi: v)
+    try:
+        test_mx_quantizer_bruteforce_tiny()
+    except (AssertionError, ValueError):
+        failures += 1
+    monkeypatch.setattr(o.np, "clip", real_clip)
+    assert failures == 3
