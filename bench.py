@@ -5,7 +5,8 @@
 A step is one call of the grouped GEMM (tile scheduling, LDS-staged scaled-MFMA
 K-loop and epilogue, all inside the one kernel) over one batch of seeded
 synthetic inputs already resident in HBM (for a gemm1 workload, such as
-kimi_tp4_gemm1_t4096, the call with the fused silu_mul epilogue); quantization happens before timing,
+kimi_tp4_gemm1_t4096, the call with the fused silu_mul epilogue; for an mx_*
+workload, the MXFP8 GEMM with one scale per 32 K elements); quantization happens before timing,
 as the inputs of the op are FP8 bytes and E8M0 scales.  Several input sets
 whose combined size exceeds the 256 MB Infinity Cache rotate between steps, so
 each step streams its operands from HBM.
@@ -51,6 +52,8 @@ def algorithmic_bytes(w, layout=None) -> int:
     KB, NB = w.K // 128, w.N // 128
     out_b = 2
     out_cols = w.I if w.op == "silu_mul" else w.N
+    a_scale_per_row = w.K // 32 if w.op == "mx" else KB
+    b_scale = w.N * (w.K // 32) if w.op == "mx" else NB * KB
     if w.layout == "masked":
         tiles_rows = sum(-(-min(max(m, 0), w.M_max) // 128) * 128 for m in w.masked_m)
         a_rows = sum(min(max(m, 0), w.M_max) for m in w.masked_m)
@@ -59,7 +62,7 @@ def algorithmic_bytes(w, layout=None) -> int:
         tiles_rows = w.M
         a_rows = w.M
         groups = sum(1 for m in w.m_per_group if m > 0)
-    return int(a_rows * w.K + tiles_rows * KB + groups * (w.N * w.K + NB * KB)
+    return int(a_rows * w.K + tiles_rows * a_scale_per_row + groups * (w.N * w.K + b_scale)
                + w.m_valid * out_cols * out_b)
 
 
@@ -130,6 +133,29 @@ def cpu_baseline(w, x):
     from threadpoolctl import threadpool_info
     from oracle import fp8_oracle as o
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    if w.op == "mx" and w.b_distinct:
+        n_exp = min(16, w.G)
+        layout = x["grouped_layout"]
+        rows = np.nonzero((layout >= 0) & (layout < n_exp))[0]
+        qa, sa = o.quantize_mx_1x32(x["a"][rows])
+        qb_d, sb_d = o.quantize_mx_1x32(x["b"])
+        sel = x["b_index"][:n_exp]
+        t0 = time.perf_counter()
+        o.grouped_gemm_mx_contiguous(qa, sa, qb_d[sel], sb_d[sel], layout[rows])
+        dt = time.perf_counter() - t0
+        flops = 2 * rows.size * w.N * w.K
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"the rows of experts 0..{n_exp - 1} of {w.name} ({rows.size} of {w.m_valid} valid rows; "
+                          f"fp64 MX dequantize + matmul), {dt:.2f} s; quantization untimed"}
+    if w.op == "mx":
+        qa, sa = o.quantize_mx_1x32(x["a"])
+        qb, sb = o.quantize_mx_1x32(x["b"])
+        t0 = time.perf_counter()
+        o.grouped_gemm_mx_contiguous(qa, sa, qb, sb, x["grouped_layout"])
+        dt = time.perf_counter() - t0
+        return {"value": round(w.flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"one full step of {w.name} (fp64 MX dequantize + matmul over all valid rows), "
+                          f"{dt:.2f} s; quantization untimed"}
     if w.op == "silu_mul":
         # bounded sample: the rows of the first 16 experts (the full weight set
         # would be 22 GB in float64)
@@ -295,15 +321,16 @@ def main():
         x = wl.draw(w, seed_offset=s)
         if s == 0:
             x0 = x
+        mx = w.op == "mx"
         if w.layout == "masked":
-            qa, sa = gfg.fp8_quantize_act_masked(x["a"])
+            qa, sa = gfg.fp8_quantize_mx_1x32(x["a"]) if mx else gfg.fp8_quantize_act_masked(x["a"])
             meta = torch.from_numpy(np.asarray(w.masked_m, np.int32)).to(dev)
             M_rows = w.G * w.M_max
         else:
-            qa, sa = gfg.fp8_quantize_act_1x128(x["a"])
+            qa, sa = gfg.fp8_quantize_mx_1x32(x["a"]) if mx else gfg.fp8_quantize_act_1x128(x["a"])
             meta = torch.from_numpy(x["grouped_layout"]).to(dev)
             M_rows = w.M
-        qb, sb = gfg.fp8_quantize_weight_128x128(x["b"])
+        qb, sb = gfg.fp8_quantize_mx_1x32(x["b"]) if mx else gfg.fp8_quantize_weight_128x128(x["b"])
         b_dev, sb_dev = torch.from_numpy(qb).to(dev), torch.from_numpy(sb).to(dev)
         if w.b_distinct:      # every expert its own copy in device memory
             idx = torch.from_numpy(x["b_index"]).to(dev)
@@ -325,14 +352,16 @@ def main():
     for t in sets:
         silu = w.op == "silu_mul"
         n_arg = w.I if silu else w.N      # the silu_mul entry points take I (B has 2*I rows)
+        fns = {"gemm": (gfg.raw_contiguous, gfg.raw_masked), "silu_mul": (gfg.raw_silu_mul_contiguous,
+               gfg.raw_silu_mul_masked), "mx": (gfg.raw_mx_contiguous, gfg.raw_mx_masked)}[w.op]
         if w.layout == "masked":
             a = (t["a"].data_ptr(), t["sa"].data_ptr(), t["b"].data_ptr(), t["sb"].data_ptr(),
                  t["meta"].data_ptr(), t["d"].data_ptr(), w.G, w.M_max, n_arg, w.K, out_code, handle)
-            calls.append((gfg.raw_silu_mul_masked if silu else gfg.raw_masked, a))
+            calls.append((fns[1], a))
         else:
             a = (t["a"].data_ptr(), t["sa"].data_ptr(), t["b"].data_ptr(), t["sb"].data_ptr(),
                  t["meta"].data_ptr(), t["d"].data_ptr(), w.M, n_arg, w.K, w.G, out_code, handle)
-            calls.append((gfg.raw_silu_mul_contiguous if silu else gfg.raw_contiguous, a))
+            calls.append((fns[0], a))
 
     def step(i):
         fn, a = calls[i % len(calls)]

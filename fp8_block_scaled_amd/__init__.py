@@ -13,7 +13,8 @@ DeepGEMM API": a contiguous layout (``grouped_layout`` maps rows to experts,
 FP8 E4M3 operands with (1,128) activation and (128,128) weight E8M0 scales.
 Both layouts also come as gemm1 of the expert MLP with its silu_mul epilogue
 (third reference page, the MoE gemm1/gemm2 pull request, section "Changes"):
-``out = silu(gate) * up`` with gate and up the two halves of ``A . B[g]^T``.
+``out = silu(gate) * up`` with gate and up the two halves of ``A . B[g]^T``,
+and as an MXFP8 GEMM (one E8M0 scale per 32 K elements of every row of A and B).
 """
 from __future__ import annotations
 
@@ -28,6 +29,8 @@ __all__ = [
     "fp8_quantize_act_1x128_device", "raw_contiguous", "raw_masked", "raw_quantize_act_device",
     "grouped_fp8_gemm_silu_mul_contiguous", "grouped_fp8_gemm_silu_mul_masked",
     "raw_silu_mul_contiguous", "raw_silu_mul_masked",
+    "grouped_mxfp8_gemm_contiguous", "grouped_mxfp8_gemm_masked", "fp8_quantize_mx_1x32",
+    "raw_mx_contiguous", "raw_mx_masked",
     "OUT_BF16", "OUT_F16", "IN_F32", "IN_BF16",
 ]
 
@@ -62,6 +65,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.grouped_fp8_gemm_silu_mul_contiguous.restype = ctypes.c_int
     lib.grouped_fp8_gemm_silu_mul_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
     lib.grouped_fp8_gemm_silu_mul_masked.restype = ctypes.c_int
+    lib.grouped_mxfp8_gemm_contiguous.argtypes = [vp, u8p, vp, u8p, vp, vp, i64, i64, i64, i32, i32, vp]
+    lib.grouped_mxfp8_gemm_contiguous.restype = ctypes.c_int
+    lib.grouped_mxfp8_gemm_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
+    lib.grouped_mxfp8_gemm_masked.restype = ctypes.c_int
+    lib.fp8_quantize_mx_1x32.argtypes = [vp, i32, i64, i64, vp, vp]
+    lib.fp8_quantize_mx_1x32.restype = ctypes.c_int
     lib.fp8_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp]
     lib.fp8_quantize_act_1x128.restype = ctypes.c_int
     lib.fp8_quantize_weight_128x128.argtypes = [vp, i32, i64, i64, vp, vp]
@@ -102,6 +111,16 @@ def raw_silu_mul_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, I, K, 
 def raw_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, I, K, out_dtype, stream=0) -> int:
     return load_library().grouped_fp8_gemm_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d,
                                                            G, M_max, I, K, out_dtype, stream)
+
+
+def raw_mx_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out_dtype, stream=0) -> int:
+    return load_library().grouped_mxfp8_gemm_contiguous(a, a_scale, b, b_scale, grouped_layout, d,
+                                                        M, N, K, G, out_dtype, stream)
+
+
+def raw_mx_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, stream=0) -> int:
+    return load_library().grouped_mxfp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d,
+                                                    G, M_max, N, K, out_dtype, stream)
 
 
 def raw_quantize_act_device(x, in_dtype, G, M, K, q, scale_t, stream=0) -> int:
@@ -238,6 +257,48 @@ def grouped_fp8_gemm_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d, stream
     return d
 
 
+def grouped_mxfp8_gemm_contiguous(a, a_scale, b, b_scale, grouped_layout, d, stream=None):
+    """MXFP8 contiguous grouped GEMM: a [M, K] e4m3 with a_scale [K/32, M], b [G, N, K] with
+    b_scale [G, K/32, N] (one E8M0 byte per 32 K elements of a row), d [M, N]."""
+    torch = _torch()
+    dev = d.device
+    f8 = (torch.uint8, torch.float8_e4m3fn)
+    M, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K or tuple(d.shape) != (M, N) or tuple(grouped_layout.shape) != (M,):
+        raise ValueError("shape mismatch between a, b, grouped_layout and d")
+    if K % 32 or tuple(a_scale.shape) != (K // 32, M) or tuple(b_scale.shape) != (G, K // 32, N):
+        raise ValueError("scale tensor shapes do not match the MX (1,32) layouts")
+    _check(raw_mx_contiguous(
+        _dev_ptr(a, "a", f8, dev), _dev_ptr(a_scale, "a_scale", (torch.uint8,), dev),
+        _dev_ptr(b, "b", f8, dev), _dev_ptr(b_scale, "b_scale", (torch.uint8,), dev),
+        _dev_ptr(grouped_layout, "grouped_layout", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev),
+        M, N, K, G, _out_code(d), _stream_handle(stream, dev)))
+    return d
+
+
+def grouped_mxfp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d, stream=None):
+    """MXFP8 masked grouped GEMM: a [G, M_max, K] with a_scale [G, K/32, M_max], b [G, N, K]
+    with b_scale [G, K/32, N], masked_m [G] int32 (device), d [G, M_max, N]."""
+    torch = _torch()
+    dev = d.device
+    f8 = (torch.uint8, torch.float8_e4m3fn)
+    G, Mmax, K = a.shape
+    Gb, N, Kb = b.shape
+    if Gb != G or Kb != K or tuple(d.shape) != (G, Mmax, N) or tuple(masked_m.shape) != (G,):
+        raise ValueError("shape mismatch between a, b, masked_m and d")
+    if K % 32 or tuple(a_scale.shape) != (G, K // 32, Mmax) or tuple(b_scale.shape) != (G, K // 32, N):
+        raise ValueError("scale tensor shapes do not match the MX (1,32) layouts")
+    _check(raw_mx_masked(
+        _dev_ptr(a, "a", f8, dev), _dev_ptr(a_scale, "a_scale", (torch.uint8,), dev),
+        _dev_ptr(b, "b", f8, dev), _dev_ptr(b_scale, "b_scale", (torch.uint8,), dev),
+        _dev_ptr(masked_m, "masked_m", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev),
+        G, Mmax, N, K, _out_code(d), _stream_handle(stream, dev)))
+    return d
+
+
 def fp8_quantize_act_1x128_device(x, q=None, scale_t=None, stream=None):
     """Per-token (1,128) ceil-E8M0 quantization on the GPU (asynchronous on ``stream``).
 
@@ -303,3 +364,16 @@ def fp8_quantize_weight_128x128(w):
     s = np.empty((G, -(-N // 128), -(-K // 128)), np.uint8)
     _check(load_library().fp8_quantize_weight_128x128(w.ctypes.data, G, N, K, q.ctypes.data, s.ctypes.data))
     return q, s
+
+
+def fp8_quantize_mx_1x32(x):
+    """MX quantization on the host: x [R, K] or [G, R, K] float32 ->
+    (q of the same shape, uint8 e4m3; scale_t [K/32, R] or [G, K/32, R], uint8 E8M0)."""
+    x = _host_f32(x, "x")
+    squeeze = x.ndim == 2
+    x3 = x[None] if squeeze else x
+    G, R, K = x3.shape
+    q = np.empty((G, R, K), np.uint8)
+    s = np.empty((G, K // 32, R), np.uint8)
+    _check(load_library().fp8_quantize_mx_1x32(x3.ctypes.data, G, R, K, q.ctypes.data, s.ctypes.data))
+    return (q[0], s[0]) if squeeze else (q, s)

@@ -135,10 +135,20 @@ __device__ __forceinline__ int scale_byte(int word, const uint8_t* row, int kb) 
 // Per-tile, per-lane constants of the K loop.  SAW: the lane's four A-scale
 // bytes (rows 4*l16 .. 4*l16+3 of its wave's 64) are read as one aligned dword
 // (scale rows a multiple of 4 bytes apart); otherwise as four bytes.
-template <int BN_, bool SAW_, bool SILU_ = false>
+template <int BN_, bool SAW_, bool SILU_ = false, bool MX_ = false>
 struct TileCtx {
     static constexpr int BN = BN_;
     static constexpr bool SAW = SAW_;
+    // MX operands: one E8M0 scale per 32 consecutive K elements of every row of
+    // A and of B, both stored transposed ([K/32][rows]).  The scaled MFMA takes
+    // a lane's 32 bytes as K [16lq, 16lq + 16) and [64 + 16lq, 80 + 16lq) of its
+    // row (logical chunks lq and lq + 4, as loaded) and applies to K-block b
+    // (K [32b, 32b + 32)) the scale of lane group b (measured on gfx950 with a
+    // one-hot probe).  So lane group lq carries the scales of block 4*kb + lq:
+    // one dword per lane and operand, bytes y (A) or x (B) picked by op_sel,
+    // and B is staged like A (fragment rows 4*l16 + x) so that a lane's four B
+    // rows are adjacent in the transposed scale layout.
+    static constexpr bool MX = MX_;
     // gemm1 with silu_mul: the B tile holds gate and up rows, and fragments
     // x < FN/2 (gate) take the gate block's scale, x >= FN/2 (up) the up block's
     static constexpr bool SILU = SILU_;
@@ -152,7 +162,7 @@ struct TileCtx {
     // vector-memory loads one wave issues per stage: DMAs and the A scales (one
     // dword or FM bytes); the B-scale dword is a scalar load
     static constexpr int SA_LOADS = SAW ? 1 : FM;
-    static constexpr int LOADS = A_DMA + B_DMA + SA_LOADS;
+    static constexpr int LOADS = A_DMA + B_DMA + SA_LOADS + (MX ? 1 : 0);   // MX: + the B-scale dword
 
     // Buffer resources (scalar registers): base + byte count.  The hardware
     // returns zero for any offset past the count instead of touching memory.
@@ -161,14 +171,18 @@ struct TileCtx {
     __amdgpu_buffer_rsrc_t sa_rsrc;   // scale_a from row m0 of K-block 0 to the region's end
     const uint8_t* sb_row;            // scale_b row (all K-blocks) of this wave's 128-column block
     const uint8_t* sbu_row;           // SILU: scale_b row of the up block (sb_row: the gate block)
-    uint32_t sa_stride;        // scale_a bytes between K-blocks (rows of the region)
+    uint32_t sa_stride;        // scale_a bytes between 128-wide K steps
+    __amdgpu_buffer_rsrc_t sb_rsrc;   // MX: scale_b of expert g from column n0 of block 0
+    uint32_t sb_off, sb_stride;       // MX: this lane's B-scale dword offset, bytes per K step
     uint32_t a_off[A_DMA];     // per-lane source offsets of this wave's DMA chunks
     uint32_t b_off[B_DMA];
     uint32_t sa_off[4];        // A-scale byte offsets (SAW: [0] only, the dword)
     // LDS byte offsets of this lane's fragment rows, logical chunks lq (lo) and
     // lq + 4 (hi).  A fragment y sits at a_*_e + y*BK for even y and at
     // a_*_o + y*BK for odd y (the row-parity exchange of the A layout).
+    // (MX: B rows as A's, at b_*_e / b_*_o.)
     int a_lo_e, a_lo_o, a_hi_e, a_hi_o, b_lo, b_hi;
+    int b_lo_e, b_lo_o, b_hi_e, b_hi_o;
 };
 
 template <int BN>
@@ -202,7 +216,10 @@ template <class C>
 __device__ __forceinline__ void issue_stage(const C& c, GFG_LDS uint8_t* __restrict__ dst,
                                             int kb, int wave, int (&sa)[4], int& sb, int& sbu) {
     load_sa(c, kb, sa);
-    sb = load_scale_word(c.sb_row, kb);
+    if constexpr (C::MX)
+        sb = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off, uint32_t(kb) * c.sb_stride, 0));
+    else
+        sb = load_scale_word(c.sb_row, kb);
     if constexpr (C::SILU) sbu = load_scale_word(c.sbu_row, kb);
     // K-block base pointers made opaque scalars, so each DMA address is a scalar
     // base plus this lane's 32-bit offset (no per-lane 64-bit induction variables)
@@ -218,9 +235,19 @@ __device__ __forceinline__ void issue_stage(const C& c, GFG_LDS uint8_t* __restr
                                          (GFG_LDS void*)(dst + C::A_BYTES + (j * C::WAVES + wave) * 1024), 16, 0, 0);
 }
 
+// LDS offset (from the B tile) of B fragment x's chunk for this lane: row
+// 16x + l16 of the wave's WN, or with MX row 4*l16 + x in the A-style layout.
+template <class C>
+__device__ __forceinline__ int b_frag(const C& c, int x, bool hi) {
+    if constexpr (C::MX)
+        return (hi ? ((x & 1) ? c.b_hi_o : c.b_hi_e) : ((x & 1) ? c.b_lo_o : c.b_lo_e)) + x * BK;
+    else
+        return (hi ? c.b_hi : c.b_lo) + x * 16 * BK;
+}
+
 // Read this lane's fragments of one stage from LDS.  A fragment (16 rows x 128 K):
 // lane (l16, lq) holds one row's 16-byte chunks lq and lq + 4; A fragment y
-// takes row 4*l16 + y of the wave's 64 rows, B fragment x row 16x + l16 of its WN.
+// takes row 4*l16 + y of the wave's 64 rows, B fragment x the row b_frag() names.
 template <class C>
 __device__ __forceinline__ void read_frags(const C& c, const GFG_LDS uint8_t* __restrict__ src,
                                            Frags<C::BN>& f) {
@@ -232,20 +259,22 @@ __device__ __forceinline__ void read_frags(const C& c, const GFG_LDS uint8_t* __
     }
 #pragma unroll
     for (int x = 0; x < C::FN; ++x) {
-        const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + C::A_BYTES + c.b_lo + x * 16 * BK);
-        const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + C::A_BYTES + c.b_hi + x * 16 * BK);
+        const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + C::A_BYTES + b_frag(c, x, false));
+        const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + C::A_BYTES + b_frag(c, x, true));
         f.b[x] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 }
 
 // MFMAs of A fragment Y against every B fragment: the A scale is byte Y of
 // the packed word (op_sel picks it), the B scale the wave's byte.
-template <class C, int Y>
+// (MX: the B scale is byte X of the lane's dword, the scale of its row 4*l16 + X.)
+template <class C, int Y, int X = 0>
 __device__ __forceinline__ void mfma_row(const Frags<C::BN>& f, int saw, int sb, int sbu, v4f (&acc)[C::FN][4]) {
-#pragma unroll
-    for (int x = 0; x < C::FN; ++x)
-        acc[x][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            f.b[x], f.a[Y], acc[x][Y], 0, 0, 0, (C::SILU && x >= C::FN / 2) ? sbu : sb, Y, saw);
+    if constexpr (X < C::FN) {
+        acc[X][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            f.b[X], f.a[Y], acc[X][Y], 0, 0, C::MX ? X : 0, (C::SILU && X >= C::FN / 2) ? sbu : sb, Y, saw);
+        mfma_row<C, Y, X + 1>(f, saw, sb, sbu, acc);
+    }
 }
 
 template <class C>
@@ -291,7 +320,7 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
     // nothing that reads this step's scale registers may rise above the wait
     __builtin_amdgcn_sched_barrier(0);
     const int sa_use = sa_word<C>(sa);
-    const int sb_use = scale_byte(sb, c.sb_row, kb_cur);
+    const int sb_use = C::MX ? sb : scale_byte(sb, c.sb_row, kb_cur);
     const int sbu_use = C::SILU ? scale_byte(sbu, c.sbu_row, kb_cur) : sb_use;
     // The LDS DMA and the fragment reads are issued here, through this
     // function's restrict parameters, so the compiler knows the refilled
@@ -319,19 +348,22 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
         }
 #pragma unroll
         for (int x = 0; x < C::FN; ++x) {
-            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + c.b_lo + x * 16 * BK);
-            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + c.b_hi + x * 16 * BK);
+            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + b_frag(c, x, false));
+            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + b_frag(c, x, true));
             nxt.b[x] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     }
     mfma_stage<C>(cur, sa_use, sb_use, sbu_use, acc);
     if (ISSUE) {   // after the MFMAs that read the old scale registers
         load_sa(c, kb_refill, sa);
-        sb = load_scale_word(c.sb_row, kb_refill);
+        if constexpr (C::MX)
+            sb = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off, uint32_t(kb_refill) * c.sb_stride, 0));
+        else
+            sb = load_scale_word(c.sb_row, kb_refill);
         if constexpr (C::SILU) sbu = load_scale_word(c.sbu_row, kb_refill);
     }
     sched_pattern<0, C::FN * C::FM, ISSUE ? C::A_DMA + C::B_DMA : 0, READ ? 2 * (C::FM + C::FN) : 0,
-                  ISSUE ? C::SA_LOADS : 0>();
+                  ISSUE ? C::SA_LOADS + (C::MX ? 1 : 0) : 0>();
     if (READ) cur = nxt;
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -356,10 +388,11 @@ __device__ __forceinline__ v4f silu_mul4(v4f gv, v4f uv) {
 // as its 256 B rows, interleaved so that each wave's 64 columns are 32 gate
 // and the same 32 up columns: fragments x and x + FN/2 of a lane then hold the
 // gate and up values of the same four outputs.
-template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU>
+template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU, bool MX>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p) {
     static_assert(!SILU || BN == 256, "the gate/up interleave assumes 64 B rows per wave");
-    using C = TileCtx<BN, SAW, SILU>;
+    static_assert(!MX || (BN == 256 && SAW && !SILU), "MX runs on the 256-column tile with packed scale words");
+    using C = TileCtx<BN, SAW, SILU, MX>;
     constexpr int FN = C::FN, FM = C::FM, WN = C::WN;
     constexpr int L = C::LOADS;
 
@@ -418,6 +451,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
     const int KB = p.K / BK;
     const int NB = p.N / 128;
     const int n_out = SILU ? p.N / 2 : p.N;   // output row length
+    const int SKB = MX ? 4 * KB : KB;           // scale blocks along K (MX: 32 wide)
     const int wm = wave & 1, wn = wave >> 1;
     const int l16 = lane & 15, lq = lane >> 4;
     GFG_LDS uint8_t* const buf0 = (GFG_LDS uint8_t*)smem0;
@@ -448,7 +482,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             g = cand / p.mt_per_group;
             m0 = int64_t(cand - g * p.mt_per_group) * BM;
             a_reg = p.a + int64_t(g) * p.rows * p.K;
-            sa_reg = p.a_scale + int64_t(g) * KB * p.rows;
+            sa_reg = p.a_scale + int64_t(g) * SKB * p.rows;
             d_reg = reinterpret_cast<uint8_t*>(p.d) + int64_t(g) * p.rows * n_out * int64_t(sizeof(OutT));
             mlimit = int(m0) + aux;
         } else {
@@ -465,14 +499,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         C c;
         c.a_tile = a_reg + m0 * p.K;
         c.b_tile = p.b + (int64_t(g) * p.N + n0) * p.K;
-        c.sa_rsrc = make_rsrc(sa_reg + m0, uint32_t(int64_t(KB) * p.rows - m0));
-        if constexpr (SILU) {
+        c.sa_rsrc = make_rsrc(sa_reg + m0, uint32_t(int64_t(SKB) * p.rows - m0));
+        if constexpr (MX) {
+            // scale_b [G][K/32][N]: this lane's dword holds rows n0 + wn*WN +
+            // 4*l16 .. +3 of block 4*kb + lq
+            const int64_t sbe = int64_t(g) * SKB * p.N;
+            c.sb_rsrc = make_rsrc(p.b_scale + sbe + n0, uint32_t(int64_t(SKB) * p.N - n0));
+            c.sb_off = uint32_t(lq * p.N + wn * WN + 4 * l16);
+            c.sb_stride = uint32_t(4 * p.N);
+        } else if constexpr (SILU) {
             c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + n0 / 128) * KB);
             c.sbu_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n_out + n0) / 128) * KB);
         } else {
             c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB);
         }
-        c.sa_stride = uint32_t(p.rows);
+        c.sa_stride = uint32_t(MX ? 4 * p.rows : p.rows);
         // DMA chunk j of this wave fills LDS rows 8*(j*WAVES + wave) .. +7; lane i
         // writes physical chunk i%8 of tile row R = +i/8, which holds logical
         // chunk (i%8) ^ key(R) of that row (A: key (R >> 2) & 7, B: R & 7).
@@ -492,8 +533,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
                 // SILU: LDS rows 64w .. 64w+31 hold gate rows o0 + 32w .., rows
                 // 64w+32 .. 64w+63 the up rows I + o0 + 32w .. (B rows from n0)
                 const int w = R >> 6, q = R & 63;
-                const int brow = !SILU ? R : (q < 32 ? 32 * w + q : n_out + 32 * w + (q - 32));
-                c.b_off[j] = uint32_t(brow) * uint32_t(p.K) + uint32_t((pc ^ rr) * 16);
+                if constexpr (MX) {   // staged like A: row a_row(R), key (R >> 2) & 7
+                    c.b_off[j] = uint32_t(a_row(R)) * uint32_t(p.K) + uint32_t((pc ^ ((R >> 2) & 7)) * 16);
+                } else {
+                    const int brow = !SILU ? R : (q < 32 ? 32 * w + q : n_out + 32 * w + (q - 32));
+                    c.b_off[j] = uint32_t(brow) * uint32_t(p.K) + uint32_t((pc ^ rr) * 16);
+                }
             }
         }
         // A-scale offsets (from row m0 of K-block 0): the lane's rows are
@@ -501,7 +546,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         // aligned fours that are all valid or all past the region's end, where
         // the buffer read returns 0 (such rows are never stored).
         if constexpr (SAW) {
-            c.sa_off[0] = uint32_t(wm * 64 + 4 * l16);
+            // (MX: block 4*kb + lq of the lane's 32-wide K chunk)
+            c.sa_off[0] = uint32_t((MX ? lq * int(p.rows) : 0) + wm * 64 + 4 * l16);
         } else {
 #pragma unroll
             for (int f = 0; f < FM; ++f) {
@@ -513,12 +559,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         // fragment rows: A row wm*64 + 4*l16 + y lives in LDS row p0 + (y ^ odd)
         // with p0 = wm*64 + 4*l16 and odd = l16 & 1 (swizzle key l16 & 7 for
         // every y); B row wn*WN + x*16 + l16 (key l16 & 7).
+        // (MX: B rows wn*WN + 4*l16 + x in LDS rows pb + (x ^ odd), as for A)
         {
+            const int clo = lq, chi = lq + 4;
             const int p0 = wm * 64 + 4 * l16, odd = l16 & 1;
-            c.a_lo_e = swz_a(p0, lq) + odd * BK;          // even y: row p0 + odd + y
-            c.a_lo_o = swz_a(p0, lq) - odd * BK;          // odd y: row p0 - odd + y
-            c.a_hi_e = swz_a(p0, lq + 4) + odd * BK;
-            c.a_hi_o = swz_a(p0, lq + 4) - odd * BK;
+            c.a_lo_e = swz_a(p0, clo) + odd * BK;          // even y: row p0 + odd + y
+            c.a_lo_o = swz_a(p0, clo) - odd * BK;          // odd y: row p0 - odd + y
+            c.a_hi_e = swz_a(p0, chi) + odd * BK;
+            c.a_hi_o = swz_a(p0, chi) - odd * BK;
+            const int pb = wn * WN + 4 * l16;
+            c.b_lo_e = swz_a(pb, clo) + odd * BK;
+            c.b_lo_o = swz_a(pb, clo) - odd * BK;
+            c.b_hi_e = swz_a(pb, chi) + odd * BK;
+            c.b_hi_o = swz_a(pb, chi) - odd * BK;
         }
         c.b_lo = swz(wn * WN + l16, lq);
         c.b_hi = swz(wn * WN + l16, lq + 4);
@@ -577,7 +630,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             const int row = int(m0) + wm * 64 + 4 * l16 + y;   // rows of a region fit in 32 bits
             const bool ok = row < mlimit && (MASKED || int(lay[y]) == g);
             if (!ok) continue;
-            if constexpr (SILU) {
+            if constexpr (MX) {
+                // lane holds columns wn*WN + 16lq + 4i + x: value acc[x][y][i]
+                typedef OutT out8 __attribute__((ext_vector_type(8)));
+                OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * p.N + n0 + wn * WN + 16 * lq;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const v4f c0 = acc[0][y], c1 = acc[1][y], c2 = acc[2][y], c3 = acc[3][y];
+                    typedef float f8v __attribute__((ext_vector_type(8)));
+                    const f8v v = {c0[2 * h], c1[2 * h], c2[2 * h], c3[2 * h],
+                                   c0[2 * h + 1], c1[2 * h + 1], c2[2 * h + 1], c3[2 * h + 1]};
+                    *reinterpret_cast<out8*>(drow + 8 * h) = __builtin_convertvector(v, out8);
+                }
+            } else if constexpr (SILU) {
                 OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * n_out + n0 + wn * (WN / 2) + 4 * lq;
 #pragma unroll
                 for (int x = 0; x < FN / 2; ++x)
@@ -617,7 +682,7 @@ int device_info(DeviceInfo* out) {
     return GFG_OK;
 }
 
-template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU = false>
+template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU = false, bool MX = false>
 int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     DeviceInfo di;
     if (int rc = device_info(&di)) return rc;
@@ -626,7 +691,8 @@ int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     unsigned grid = upper < unsigned(di.cus) ? upper : unsigned(di.cus);
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;          // whole slots on every XCD
     if (grid == 0) return GFG_OK;
-    hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, SAW, OutT, SILU>), dim3(grid), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, SAW, OutT, SILU, MX>), dim3(grid), dim3(NTHREADS), 0, s,
+                       p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(GFG_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GFG_OK;
@@ -734,6 +800,24 @@ int check_silu(const char* fn, int64_t I, int64_t rows, const uint8_t* a_scale) 
     return GFG_OK;
 }
 
+// The MX GEMM runs on the 256-column tile with one scale dword per lane and
+// operand: N a multiple of 256, scale rows a multiple of 4, both scale
+// tensors 4-byte aligned.
+int check_mx(const char* fn, int64_t N, int64_t rows, const uint8_t* a_scale, const uint8_t* b_scale) {
+    if (N % 256) return fail(GFG_EUNSUPPORTED, "%s: N=%lld must be a multiple of 256", fn, (long long)N);
+    if (rows % 4 || reinterpret_cast<uintptr_t>(a_scale) % 4 || reinterpret_cast<uintptr_t>(b_scale) % 4)
+        return fail(GFG_EUNSUPPORTED,
+                    "%s: needs scale_a rows (%lld) a multiple of 4 and both scale tensors 4-byte aligned", fn,
+                    (long long)rows);
+    return GFG_OK;
+}
+
+template <bool MASKED>
+int dispatch_mx(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
+    return out_dtype == GFG_OUT_BF16 ? launch_t<256, MASKED, true, __bf16, false, true>(p, n_cand, s)
+                                     : launch_t<256, MASKED, true, _Float16, false, true>(p, n_cand, s);
+}
+
 template <bool MASKED>
 int dispatch_silu(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
     return out_dtype == GFG_OUT_BF16 ? launch_t<256, MASKED, true, __bf16, true>(p, n_cand, s)
@@ -800,4 +884,33 @@ extern "C" int grouped_fp8_gemm_silu_mul_masked(const void* a, const uint8_t* a_
         return rc;
     if (M_max == 0) return GFG_OK;
     return dispatch_silu<true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int grouped_mxfp8_gemm_contiguous(const void* a, const uint8_t* a_scale, const void* b,
+                                             const uint8_t* b_scale, const int32_t* grouped_layout, void* d,
+                                             int64_t M, int64_t N, int64_t K, int32_t G, int32_t out_dtype,
+                                             void* stream) {
+    clear_error();
+    const char* fn = "grouped_mxfp8_gemm_contiguous";
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out_dtype, &p, &n_cand))
+        return rc;
+    if (int rc = check_mx(fn, N, M, a_scale, b_scale)) return rc;
+    if (M == 0) return GFG_OK;
+    return dispatch_mx<false>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int grouped_mxfp8_gemm_masked(const void* a, const uint8_t* a_scale, const void* b,
+                                         const uint8_t* b_scale, const int32_t* masked_m, void* d, int32_t G,
+                                         int64_t M_max, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
+    clear_error();
+    const char* fn = "grouped_mxfp8_gemm_masked";
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, &p, &n_cand))
+        return rc;
+    if (int rc = check_mx(fn, N, M_max, a_scale, b_scale)) return rc;
+    if (M_max == 0) return GFG_OK;
+    return dispatch_mx<true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
 }

@@ -62,6 +62,20 @@ bool ceil_e8m0(float amax, int* t) {
     return true;
 }
 
+// MX scale exponent for E4M3 elements: t = floor(log2(amax)) - 8, so the
+// scaled block's largest magnitude lies in [256, 512) (E4M3's top binade; the
+// values above 448 saturate).  frexp is exact for normal and subnormal amax.
+bool mx_floor_e8m0(float amax, int* t) {
+    if (!(amax >= 0.0f) || std::isinf(amax)) return false;
+    if (amax == 0.0f) { *t = 0; return true; }
+    int p;
+    std::frexp(amax, &p);                  // amax = f * 2^p, f in [0.5, 1): floor(log2) = p - 1
+    const int tt = p - 1 - 8;
+    if (tt < -127 || tt > 127) return false;
+    *t = tt;
+    return true;
+}
+
 // Nearest E4M3FN code of v (|v| <= 448), ties to the even mantissa.
 inline uint8_t e4m3_rne(float v) {
     uint32_t u = f2u(v);
@@ -167,5 +181,42 @@ extern "C" int fp8_quantize_weight_128x128(const float* w, int32_t G, int64_t N,
         if (bad[size_t(i)])
             return fail(GFG_ERANGE, "fp8_quantize_weight_128x128: block row %lld has a block outside the "
                         "E8M0 range or a non-finite value", (long long)i);
+    return GFG_OK;
+}
+
+extern "C" int fp8_quantize_mx_1x32(const float* x, int32_t G, int64_t R, int64_t K, uint8_t* q,
+                                    uint8_t* scale_t) {
+    clear_error();
+    const char* fn = "fp8_quantize_mx_1x32";
+    if (G <= 0 || R < 0 || K <= 0)
+        return fail(GFG_EINVAL, "%s: bad sizes G=%d R=%lld K=%lld", fn, G, (long long)R, (long long)K);
+    if (K % 32) return fail(GFG_EUNSUPPORTED, "%s: K=%lld must be a multiple of 32", fn, (long long)K);
+    if (R == 0) return GFG_OK;
+    if (!x || !q || !scale_t) return fail(GFG_EINVAL, "%s: null pointer", fn);
+    const int64_t KB = K / 32;
+    std::vector<int> bad(size_t(G * R), 0);
+    parallel_for(int64_t(G) * R, [&](int64_t gr) {
+        const int64_t g = gr / R, r = gr % R;
+        const float* row = x + gr * K;
+        for (int64_t j = 0; j < KB; ++j) {
+            float amax = 0.0f;
+            bool nan = false;
+            for (int64_t k = 32 * j; k < 32 * j + 32; ++k) {
+                amax = std::max(amax, std::fabs(row[k]));
+                nan |= row[k] != row[k];
+            }
+            int t;
+            if (nan || !mx_floor_e8m0(amax, &t)) { bad[size_t(gr)] = 1; return; }
+            scale_t[(g * KB + j) * R + r] = uint8_t(t + 127);
+            for (int64_t k = 32 * j; k < 32 * j + 32; ++k) {
+                const float v = std::ldexp(row[k], -t);
+                q[gr * K + k] = e4m3_rne(std::min(448.0f, std::max(-448.0f, v)));
+            }
+        }
+    });
+    for (int64_t i = 0; i < int64_t(G) * R; ++i)
+        if (bad[size_t(i)])
+            return fail(GFG_ERANGE, "%s: row %lld has a block outside the E8M0 range or a non-finite value", fn,
+                        (long long)i);
     return GFG_OK;
 }

@@ -26,6 +26,10 @@ routed to it, padded to a multiple of 128.  The 385 weight matrices are 8
 seeded N(0,1) draws repeated in turn (expert g uses draw g % 8): the kernel
 reads 385 separate copies from device memory, but the host draws and
 quantizes only 8 (11 GB of float32 otherwise).
+
+MXFP8 (the third page's MX kernels, with E4M3 elements): the same data
+recipes, quantized with one E8M0 scale per 32 K elements of every row --
+the benchmarked 4 x 1024, N=2048, K=7168 shape and the Kimi gemm1 shape.
 """
 from __future__ import annotations
 
@@ -49,7 +53,7 @@ class Workload:
     M_max: int = 0                                    # masked: rows per group buffer
     masked_m: list = field(default_factory=list)      # masked: valid rows per group
     row_log10_range: tuple | None = None              # per-token magnitude 10**U(lo, hi)
-    op: str = "gemm"                                  # "gemm" or "silu_mul" (N = 2*I)
+    op: str = "gemm"                                  # "gemm", "silu_mul" (N = 2*I) or "mx" (MXFP8)
     b_distinct: int = 0                               # > 0: expert g's B is draw g % b_distinct
 
     @property
@@ -128,6 +132,15 @@ def gemm1_workloads() -> list[Workload]:
                      m_per_group=_topk_counts(_rng(1006), 4096, 385, 9), op="silu_mul", b_distinct=8)]
 
 
+def mx_workloads() -> list[Workload]:
+    """MXFP8 GEMMs: the benchmarked contiguous shape (seed 1007, N(0,1)) and the
+    Kimi-K2.5 TP=4 gemm1 shape without its epilogue (seed 1008)."""
+    return [Workload("mx_contig_g4_m1024_n2048_k7168", "contiguous", 4, 2048, 7168, "bf16", 1007,
+                     m_per_group=[1024] * 4, op="mx"),
+            Workload("mx_kimi_tp4_gemm1_t4096", "contiguous", 385, 1024, 7168, "bf16", 1008,
+                     m_per_group=_topk_counts(_rng(1008), 4096, 385, 9), op="mx", b_distinct=8)]
+
+
 def workload(name_or_index) -> Workload:
     """A standard workload by index or name, a context workload by name, or an
     ad-hoc one named ``contig_g{G}_m{rows per group}_n{N}_k{K}`` or
@@ -140,6 +153,10 @@ def workload(name_or_index) -> Workload:
             return w
     if name_or_index.startswith("kimi_"):
         for w in gemm1_workloads():
+            if w.name == name_or_index:
+                return w
+    if name_or_index.startswith("mx_"):
+        for w in mx_workloads():
             if w.name == name_or_index:
                 return w
     import re

@@ -139,6 +139,44 @@ GFG_API int grouped_fp8_gemm_silu_mul_masked(const void* a, const uint8_t* a_sca
                                      int32_t out_dtype, void* stream);
 
 /*
+ * MXFP8 grouped GEMM: the same two layouts on MX operands (third reference
+ * page, "flydsl mxfp4 a4w4 MoE: bring gemm1/gemm2 to parity with the HIP
+ * backend", section "Notes": MX kernels with E8M0 scales; here with E4M3
+ * elements).  Every row of A and of B carries one E8M0 scale per 32
+ * consecutive K elements; the hardware applies each one to its 32 products
+ * inside the scaled MFMA.
+ *
+ *   a, b, grouped_layout / masked_m, d   as in the GEMMs above
+ *   a_scale   contiguous [K/32][M], masked [G][K/32][M_max]   (transposed, per 32-wide K block)
+ *   b_scale   [G][K/32][N]
+ *
+ * Sizes: as the GEMMs above, and N a multiple of 256, M (M_max) a multiple
+ * of 4, a_scale and b_scale 4-byte aligned (else GFG_EUNSUPPORTED).
+ */
+GFG_API int grouped_mxfp8_gemm_contiguous(const void* a, const uint8_t* a_scale,
+                                  const void* b, const uint8_t* b_scale,
+                                  const int32_t* grouped_layout, void* d,
+                                  int64_t M, int64_t N, int64_t K, int32_t G,
+                                  int32_t out_dtype, void* stream);
+GFG_API int grouped_mxfp8_gemm_masked(const void* a, const uint8_t* a_scale,
+                              const void* b, const uint8_t* b_scale,
+                              const int32_t* masked_m, void* d,
+                              int32_t G, int64_t M_max, int64_t N, int64_t K,
+                              int32_t out_dtype, void* stream);
+
+/*
+ * MX quantizer (CPU, synchronous) for the MXFP8 GEMM's operands:
+ *   x [G][R][K] float -> q [G][R][K] e4m3, scale_t [G][K/32][R] E8M0
+ * (A: G = 1, R = M; masked A: G groups of R = M_max; B: G experts of R = N).
+ * Per row and 32-wide K block: t = floor(log2(max|x|)) - 8 (t = 0 for an
+ * all-zero block), scale byte t + 127, q = E4M3(clamp(x / 2^t, -448, 448))
+ * nearest-even.  K must be a multiple of 32 (else GFG_EUNSUPPORTED);
+ * GFG_ERANGE if t falls outside [-127, 127] or a value is not finite.
+ */
+GFG_API int fp8_quantize_mx_1x32(const float* x, int32_t G, int64_t R, int64_t K,
+                         uint8_t* q, uint8_t* scale_t);
+
+/*
  * Host quantizers (CPU, synchronous), ceil-E8M0 scales and nearest-even E4M3:
  * for each block, t = the smallest integer with 448 * 2^t >= amax (t = 0 for
  * an all-zero block), scale byte = t + 127, q = E4M3(x / 2^t).  The rounding

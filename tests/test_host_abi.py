@@ -205,3 +205,81 @@ def test_silu_mul_empty_is_noop():
     assert _sm(Mmax=0) == 0
     assert _sc(M=-4) == 1
     assert _sm(Mmax=-4) == 1
+
+
+# ------------------------------------------------------------------ MXFP8
+@pytest.mark.parametrize("shape", [(1, 32), (7, 96), (65, 256), (3, 40, 128)])
+def test_mx_quantizer_bit_exact(shape):
+    rng = np.random.default_rng(sum(shape))
+    x = (rng.standard_normal(shape) * 10.0 ** rng.uniform(-4, 4, shape[:-1] + (1,))).astype(np.float32)
+    q, s = gfg.fp8_quantize_mx_1x32(x)
+    oq, os_ = o.quantize_mx_1x32(x)
+    assert np.array_equal(q, oq) and np.array_equal(s, os_)
+
+
+def test_mx_quantizer_boundaries_bit_exact():
+    """Blocks at the exponent edges (amax = 256*2^t, one ulp below, 512*2^t),
+    saturating blocks (scaled maximum in (448, 512)), subnormal elements, an
+    all-zero block and negative zeros."""
+    blocks = []
+    for t in (-30, -1, 0, 5, 60):
+        for amax in (256.0 * 2.0 ** t, np.nextafter(256.0 * 2.0 ** t, 0), 500.0 * 2.0 ** t, 448.0 * 2.0 ** t):
+            b = np.linspace(-1, 1, 32) * amax
+            b[7] = amax
+            blocks.append(b)
+    z = np.zeros(32)
+    z[3] = -0.0
+    blocks.append(z)
+    tiny = np.full(32, 2.0 ** -20)
+    tiny[0] = 1.0
+    blocks.append(tiny)
+    x = np.stack(blocks).astype(np.float32).reshape(1, -1)
+    x = np.concatenate([x, -x[:, ::-1]])
+    q, s = gfg.fp8_quantize_mx_1x32(x)
+    oq, os_ = o.quantize_mx_1x32(x)
+    assert np.array_equal(s, os_) and np.array_equal(q, oq)
+
+
+def test_mx_quantizer_errors():
+    lib = gfg.load_library()
+    x = np.zeros((2, 64), np.float32)
+    q = np.empty((2, 64), np.uint8)
+    s = np.empty((2, 2), np.uint8)
+    assert lib.fp8_quantize_mx_1x32(x.ctypes.data, 1, 2, 48, q.ctypes.data, s.ctypes.data) == 2   # K % 32
+    assert lib.fp8_quantize_mx_1x32(None, 1, 2, 64, q.ctypes.data, s.ctypes.data) == 1
+    assert lib.fp8_quantize_mx_1x32(x.ctypes.data, 0, 2, 64, q.ctypes.data, s.ctypes.data) == 1
+    x[1, 40] = np.nan
+    assert lib.fp8_quantize_mx_1x32(x.ctypes.data, 1, 2, 64, q.ctypes.data, s.ctypes.data) == 4
+    x[1, 40] = 1e-37                         # t = -131
+    assert lib.fp8_quantize_mx_1x32(x.ctypes.data, 1, 2, 64, q.ctypes.data, s.ctypes.data) == 4
+
+
+def _mc(**kw):
+    args = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, meta=FAKE, d=FAKE, M=256, N=256, K=256, G=2, dt=0)
+    args.update(kw)
+    return gfg.raw_mx_contiguous(args["a"], args["sa"], args["b"], args["sb"], args["meta"], args["d"],
+                                 args["M"], args["N"], args["K"], args["G"], args["dt"], 0)
+
+
+def _mm(**kw):
+    args = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, meta=FAKE, d=FAKE, G=2, Mmax=256, N=256, K=256, dt=0)
+    args.update(kw)
+    return gfg.raw_mx_masked(args["a"], args["sa"], args["b"], args["sb"], args["meta"], args["d"],
+                             args["G"], args["Mmax"], args["N"], args["K"], args["dt"], 0)
+
+
+@pytest.mark.parametrize("fn", [_mc, _mm])
+def test_mx_gemm_argument_errors(fn):
+    for k in ("a", "sa", "b", "sb", "meta", "d"):
+        assert fn(**{k: None}) == 1, k
+    assert fn(dt=2) == 1
+    assert fn(G=0) == 1
+    assert fn(K=300) == 2
+    assert fn(N=384) == 2          # N must be a multiple of 256
+    assert "multiple of 256" in gfg.load_library().gfg_last_error().decode()
+    assert fn(sa=FAKE + 1) == 2
+    assert fn(sb=FAKE + 2) == 2
+    rows = {"M": 130} if fn is _mc else {"Mmax": 130}
+    assert fn(**rows) == 2
+    empty = {"M": 0} if fn is _mc else {"Mmax": 0}
+    assert fn(**empty) == 0
