@@ -375,6 +375,119 @@ def grouped_gemm_mx_masked(q_a, scale_a, q_b, scale_b, masked_m, d_init=None):
     return d
 
 
+# ---------------------------------------------------------------- MXFP4 (E2M1, 1 x 32 blocks)
+# The page's own element type: "mxfp4 (a4w4)" (third reference page, section
+# "Summary").  E2M1 (OCP FP4): 1 sign, 2 exponent bits (bias 1), 1 mantissa
+# bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinity or NaN.  Readings
+# of what the page leaves open:
+#   * scale exponent t = floor(log2(amax)) - 2 (2 is the exponent of E2M1's
+#     largest power of two, 4); elements x / 2**t rounded to nearest, ties to
+#     the even code ("Even"), clamped to +-6; all-zero block t = 0;
+#   * two elements per byte, the lower K index in the low nibble;
+#   * scales as for MXFP8: [K/32, M] for A and [G, K/32, N] for B.
+
+E2M1_MAX = 6.0
+MX4_EMAX = 2
+
+
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Value of each 4-bit E2M1 code (0..15), float64."""
+    c = np.asarray(codes, dtype=np.int64) & 15
+    s, e, m = c >> 3, (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(s == 1, -mag, mag)
+
+
+def encode_e2m1_rne(x: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code to each value with |x| <= 6, ties to the even code.
+
+    The positive codes 0..7 are in increasing order of value, so the nearest
+    code is found by comparing against the midpoints between neighbours; a
+    value exactly on a midpoint takes the code with an even mantissa bit.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E2M1_MAX) or np.any(~np.isfinite(x)):
+        raise ValueError("encode_e2m1_rne: |x| must be <= 6")
+    vals = decode_e2m1(np.arange(8))                     # 0, .5, 1, 1.5, 2, 3, 4, 6
+    a = np.abs(x)
+    code = np.zeros(a.shape, dtype=np.int64)
+    for c in range(7):
+        mid = (vals[c] + vals[c + 1]) / 2.0
+        up = (a > mid) | ((a == mid) & ((c + 1) % 2 == 0))
+        code = np.where(up & (code == c), c + 1, code)
+    return (code | np.where(np.signbit(x), 8, 0)).astype(np.uint8)
+
+
+def mx4_exponent(amax: np.ndarray) -> np.ndarray:
+    """t = floor(log2(amax)) - 2 exactly, 0 where amax == 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    if np.any(~np.isfinite(amax)) or np.any(amax < 0):
+        raise ValueError("mx4_exponent: amax must be finite and >= 0")
+    _, p = np.frexp(np.where(amax > 0, amax, 1.0))
+    t = np.where(amax > 0, p.astype(np.int64) - 1 - MX4_EMAX, 0)
+    if np.any(t < -127) or np.any(t > 127):
+        raise ValueError("mx4_exponent: scale outside the E8M0 range")
+    return t
+
+
+def quantize_mx4_1x32(x: np.ndarray):
+    """MXFP4 quantization of x[..., R, K] along K (K a multiple of 32).
+
+    Returns ``(q [..., R, K/2] uint8, scale_t [..., K/32, R] uint8)``: codes
+    RNE_e2m1(clamp(x / 2**t, -6, 6)) packed two per byte (element 2i in the
+    low nibble of byte i), t = mx4_exponent(max |block|) per 32-wide block.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    *lead, R, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("quantize_mx4_1x32: K must be a multiple of 32")
+    xb = x.reshape(*lead, R, K // MX_BLOCK, MX_BLOCK)
+    t = mx4_exponent(np.abs(xb).max(axis=-1))
+    v = np.clip(xb / np.exp2(t[..., None].astype(np.float64)), -E2M1_MAX, E2M1_MAX)
+    codes = encode_e2m1_rne(v).reshape(*lead, R, K)
+    q = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    st = np.swapaxes((t + 127).astype(np.uint8), -1, -2)
+    return np.ascontiguousarray(q), np.ascontiguousarray(st)
+
+
+def dequantize_mx4(q: np.ndarray, scale_t: np.ndarray) -> np.ndarray:
+    """X_dq[..., r, k] = e2m1(nibble k of row r) * 2**(scale_t[..., k // 32, r] - 127)."""
+    q = np.asarray(q, dtype=np.uint8)
+    codes = np.stack([q & 15, q >> 4], axis=-1).reshape(*q.shape[:-1], 2 * q.shape[-1])
+    s = np.swapaxes(e8m0_value(scale_t), -1, -2)
+    return decode_e2m1(codes) * np.repeat(s, MX_BLOCK, axis=-1)
+
+
+def grouped_gemm_mx4_contiguous(q_a, scale_a, q_b, scale_b, grouped_layout, d_init=None):
+    """Contiguous grouped GEMM on MXFP4 operands (A [M, K/2] packed, B [G, N, K/2]),
+    float64; other rows keep ``d_init``."""
+    a = dequantize_mx4(q_a, scale_a)
+    b = dequantize_mx4(q_b, scale_b)
+    layout = np.asarray(grouped_layout, dtype=np.int64)
+    M, N = a.shape[0], b.shape[1]
+    d = np.full((M, N), np.nan) if d_init is None else np.array(d_init, dtype=np.float64)
+    for g in range(b.shape[0]):
+        rows = np.nonzero(layout == g)[0]
+        if rows.size:
+            d[rows] = a[rows] @ b[g].T
+    return d
+
+
+def grouped_gemm_mx4_masked(q_a, scale_a, q_b, scale_b, masked_m, d_init=None):
+    """Masked grouped GEMM on MXFP4 operands: A [G, M_max, K/2] with scale_a
+    [G, K/32, M_max]; rows m < masked_m[g] computed, others keep ``d_init``."""
+    G, Mmax, _ = q_a.shape
+    b = dequantize_mx4(q_b, scale_b)
+    N = b.shape[1]
+    d = np.full((G, Mmax, N), np.nan) if d_init is None else np.array(d_init, dtype=np.float64)
+    for g in range(G):
+        mm = int(min(max(int(masked_m[g]), 0), Mmax))
+        if mm:
+            a = dequantize_mx4(q_a[g, :mm], scale_a[g][:, :mm])
+            d[g, :mm] = a @ b[g].T
+    return d
+
+
 # ---------------------------------------------------------------- metrics
 def calc_diff(x, y) -> float:
     """1 - 2*sum(x*y) / sum(x*x + y*y), in float64 ("cosine-similarity-style")."""

@@ -685,3 +685,167 @@ def test_mx_pins_catch_planted_mistakes(monkeypatch):
         failures += 1
     monkeypatch.setattr(o.np, "clip", real_clip)
     assert failures == 3
+
+
+# ------------------------------------------------------------------ MXFP4 (E2M1) pins
+def test_e2m1_decode_golden():
+    rows = _read_golden("e2m1_codes.txt")
+    codes = np.array([int(c, 16) for c, _ in rows])
+    vals = np.array([float(v) for _, v in rows])
+    got = o.decode_e2m1(codes)
+    assert np.array_equal(got, vals) and np.array_equal(np.signbit(got), np.signbit(vals))
+
+
+def _bf_e2m1(v: float) -> int:
+    """Nearest E2M1 code by exhaustive search over the 16 codes; ties to the even code."""
+    table = [(c, float(o.decode_e2m1(np.array(c)))) for c in range(16)]
+    neg = math.copysign(1.0, v) < 0
+    best = None
+    for c, val in table:
+        if val == 0.0 and bool(c >> 3) != neg:
+            continue                     # keep the sign of zero
+        key = (abs(val - v), c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def test_e2m1_encode_bruteforce():
+    rng = np.random.default_rng(51)
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    x = np.concatenate([rng.uniform(-6, 6, 3000), np.array(mids), -np.array(mids),
+                        np.array([0.0, -0.0, 6.0, -6.0, 5.999, 0.2500001, 0.2499999])])
+    got = o.encode_e2m1_rne(x)
+    want = np.array([_bf_e2m1(float(v)) for v in x])
+    assert np.array_equal(got, want)
+    with pytest.raises(ValueError):
+        o.encode_e2m1_rne(np.array([6.5]))
+
+
+def test_mx4_exponent_bruteforce():
+    rng = np.random.default_rng(52)
+    amax = np.concatenate([rng.uniform(0, 1, 400) * 10.0 ** rng.uniform(-30, 30, 400),
+                           2.0 ** rng.integers(-100, 100, 40).astype(np.float64), np.array([0.0, 4.0, 7.999, 8.0])])
+    t = o.mx4_exponent(amax)
+    for a, ti in zip(amax, t):
+        want = 0 if a == 0 else next(k for k in range(-140, 140) if 4.0 * 2.0 ** k <= a < 8.0 * 2.0 ** k)
+        assert ti == want, (a, ti, want)
+
+
+def _bf_quant_mx4(x):
+    R, K = x.shape
+    q = np.zeros((R, K // 2), np.uint8)
+    s = np.zeros((K // 32, R), np.uint8)
+    for r in range(R):
+        for j in range(K // 32):
+            blk = [float(v) for v in x[r, 32 * j:32 * j + 32]]
+            amax = max(abs(v) for v in blk)
+            t = 0 if amax == 0 else next(k for k in range(-140, 140) if 4.0 * 2.0 ** k <= amax < 8.0 * 2.0 ** k)
+            s[j, r] = t + 127
+            for i, v in enumerate(blk):
+                k = 32 * j + i
+                c = _bf_e2m1(min(max(v / 2.0 ** t, -6.0), 6.0))
+                q[r, k // 2] |= c << (4 * (k % 2))      # element 2i: low nibble of byte i
+    return q, s
+
+
+def test_mx4_quantizer_bruteforce_tiny():
+    rng = np.random.default_rng(53)
+    x = (rng.standard_normal((4, 96)) * 10.0 ** rng.uniform(-3, 3, (4, 1))).astype(np.float32)
+    x[1, 32:64] = 0.0
+    x[2, 0:32] = np.float32(7.5)        # t = 0 (4 <= 7.5 < 8): 7.5 saturates to 6
+    x[2, 3] = np.float32(-7.0)
+    q, s = o.quantize_mx4_1x32(x)
+    bq, bs = _bf_quant_mx4(x)
+    assert np.array_equal(s, bs) and np.array_equal(q, bq)
+    assert q[2, 0] == 0x77 and (q[2, 1] >> 4) == 0xF
+
+
+def test_mx4_dequantize_nibble_order():
+    """Byte 0x21 holds element 0 = code 1 (0.5) in its low nibble and element
+    1 = code 2 (1.0) in its high nibble; scale byte 128 doubles both.  (A
+    swap applied to both GEMM operands alike cancels in the dot product, so
+    the order is pinned here directly.)"""
+    q = np.zeros((1, 16), np.uint8)
+    q[0, 0] = 0x21
+    q[0, 15] = 0xF7                       # element 30 = 6.0, element 31 = -6.0
+    got = o.dequantize_mx4(q, np.array([[128]], np.uint8))
+    assert got[0, 0] == 1.0 and got[0, 1] == 2.0
+    assert got[0, 30] == 12.0 and got[0, 31] == -12.0
+    assert np.all(got[0, 2:30] == 0.0)
+
+
+def _bf_mx4_gemm_rows(qa, sa, qb, sb, rows_a, g):
+    N, Kh = qb.shape[1], qb.shape[2]
+    val = lambda byte, k: float(o.decode_e2m1(np.array((int(byte) >> (4 * (k % 2))) & 15)))
+    out = np.zeros((len(rows_a), N))
+    for i, r in enumerate(rows_a):
+        a = [val(qa[r, k // 2], k) * 2.0 ** (int(sa[k // 32, r]) - 127) for k in range(2 * Kh)]
+        for n in range(N):
+            out[i, n] = math.fsum(a[k] * val(qb[g, n, k // 2], k) * 2.0 ** (int(sb[g, k // 32, n]) - 127)
+                                  for k in range(2 * Kh))
+    return out
+
+
+def test_mx4_contiguous_gemm_bruteforce_tiny():
+    rng = np.random.default_rng(54)
+    layout = np.array([1, 1, -1, 0, 0], np.int32)
+    K, N = 64, 24
+    a = rng.standard_normal((layout.size, K)).astype(np.float32)
+    b = rng.standard_normal((2, N, K)).astype(np.float32)
+    qa, sa = o.quantize_mx4_1x32(a)
+    qb, sb = o.quantize_mx4_1x32(b)
+    assert qa.shape == (layout.size, K // 2) and sb.shape == (2, K // 32, N)
+    d = o.grouped_gemm_mx4_contiguous(qa, sa, qb, sb, layout, np.full((layout.size, N), 1.25))
+    for g in range(2):
+        rows = [r for r in range(layout.size) if layout[r] == g]
+        np.testing.assert_allclose(d[rows], _bf_mx4_gemm_rows(qa, sa, qb, sb, rows, g), rtol=1e-12, atol=1e-12)
+    assert np.all(d[layout < 0] == 1.25)
+
+
+def test_mx4_masked_gemm_bruteforce_tiny():
+    rng = np.random.default_rng(55)
+    G, Mmax, K, N = 2, 3, 64, 16
+    a = rng.standard_normal((G, Mmax, K)).astype(np.float32)
+    b = rng.standard_normal((G, N, K)).astype(np.float32)
+    masked_m = np.array([2, 3], np.int32)
+    qa, sa = o.quantize_mx4_1x32(a)
+    qb, sb = o.quantize_mx4_1x32(b)
+    d = o.grouped_gemm_mx4_masked(qa, sa, qb, sb, masked_m, np.full((G, Mmax, N), 7.0))
+    for g in range(G):
+        mm = int(masked_m[g])
+        np.testing.assert_allclose(d[g, :mm], _bf_mx4_gemm_rows(qa[g], sa[g], qb, sb, list(range(mm)), g),
+                                   rtol=1e-12, atol=1e-12)
+        assert np.all(d[g, mm:] == 7.0)
+
+
+def test_mx4_pins_catch_planted_mistakes(monkeypatch):
+    """Planted MXFP4 mistakes (on the CPU): nibbles in the wrong order, the
+    FP8 exponent rule (-8) instead of FP4's (-2), and no saturation."""
+    failures = 0
+    real_dq = o.dequantize_mx4
+
+    def swapped(q, scale_t):
+        q = np.asarray(q, np.uint8)
+        return real_dq(((q << 4) | (q >> 4)).astype(np.uint8), scale_t)
+    monkeypatch.setattr(o, "dequantize_mx4", swapped)
+    try:
+        test_mx4_dequantize_nibble_order()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "dequantize_mx4", real_dq)
+    real_exp = o.mx4_exponent
+    monkeypatch.setattr(o, "mx4_exponent", lambda a: o.mx_exponent(a))
+    try:
+        test_mx4_exponent_bruteforce()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "mx4_exponent", real_exp)
+    real_clip = np.clip
+    monkeypatch.setattr(o.np, "clip", lambda v, lo, hi: v)
+    try:
+        test_mx4_quantizer_bruteforce_tiny()
+    except (AssertionError, ValueError):
+        failures += 1
+    monkeypatch.setattr(o.np, "clip", real_clip)
+    assert failures == 3
