@@ -6,7 +6,8 @@ A step is one call of the grouped GEMM (tile scheduling, LDS-staged scaled-MFMA
 K-loop and epilogue, all inside the one kernel) over one batch of seeded
 synthetic inputs already resident in HBM (for a gemm1 workload, such as
 kimi_tp4_gemm1_t4096, the call with the fused silu_mul epilogue; for an mx_*
-workload, the MXFP8 GEMM with one scale per 32 K elements); quantization happens before timing,
+workload, the MXFP8 GEMM with one scale per 32 K elements; for mx4_*, the
+MXFP4 one, priced against the FP4 peak); quantization happens before timing,
 as the inputs of the op are FP8 bytes and E8M0 scales.  Several input sets
 whose combined size exceeds the 256 MB Infinity Cache rotate between steps, so
 each step streams its operands from HBM.
@@ -30,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA peak
+PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 (and FP6) MFMA peak
 PEAK_HBM_GBS = 8000.0
 RIDGE_FLOP_PER_BYTE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 DEFAULT_WORKLOAD = "contig_g4_m1024_n2048_k7168"
@@ -52,8 +54,10 @@ def algorithmic_bytes(w, layout=None) -> int:
     KB, NB = w.K // 128, w.N // 128
     out_b = 2
     out_cols = w.I if w.op == "silu_mul" else w.N
-    a_scale_per_row = w.K // 32 if w.op == "mx" else KB
-    b_scale = w.N * (w.K // 32) if w.op == "mx" else NB * KB
+    mx = w.op in ("mx", "mx4")
+    a_scale_per_row = w.K // 32 if mx else KB
+    b_scale = w.N * (w.K // 32) if mx else NB * KB
+    elem = 0.5 if w.op == "mx4" else 1.0          # bytes per A/B element
     if w.layout == "masked":
         tiles_rows = sum(-(-min(max(m, 0), w.M_max) // 128) * 128 for m in w.masked_m)
         a_rows = sum(min(max(m, 0), w.M_max) for m in w.masked_m)
@@ -62,7 +66,7 @@ def algorithmic_bytes(w, layout=None) -> int:
         tiles_rows = w.M
         a_rows = w.M
         groups = sum(1 for m in w.m_per_group if m > 0)
-    return int(a_rows * w.K + tiles_rows * a_scale_per_row + groups * (w.N * w.K + b_scale)
+    return int(a_rows * w.K * elem + tiles_rows * a_scale_per_row + groups * (w.N * w.K * elem + b_scale)
                + w.m_valid * out_cols * out_b)
 
 
@@ -133,25 +137,27 @@ def cpu_baseline(w, x):
     from threadpoolctl import threadpool_info
     from oracle import fp8_oracle as o
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    if w.op == "mx" and w.b_distinct:
+    quant_mx = o.quantize_mx4_1x32 if w.op == "mx4" else o.quantize_mx_1x32
+    gemm_mx = o.grouped_gemm_mx4_contiguous if w.op == "mx4" else o.grouped_gemm_mx_contiguous
+    if w.op in ("mx", "mx4") and w.b_distinct:
         n_exp = min(16, w.G)
         layout = x["grouped_layout"]
         rows = np.nonzero((layout >= 0) & (layout < n_exp))[0]
-        qa, sa = o.quantize_mx_1x32(x["a"][rows])
-        qb_d, sb_d = o.quantize_mx_1x32(x["b"])
+        qa, sa = quant_mx(x["a"][rows])
+        qb_d, sb_d = quant_mx(x["b"])
         sel = x["b_index"][:n_exp]
         t0 = time.perf_counter()
-        o.grouped_gemm_mx_contiguous(qa, sa, qb_d[sel], sb_d[sel], layout[rows])
+        gemm_mx(qa, sa, qb_d[sel], sb_d[sel], layout[rows])
         dt = time.perf_counter() - t0
         flops = 2 * rows.size * w.N * w.K
         return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                 "sample": f"the rows of experts 0..{n_exp - 1} of {w.name} ({rows.size} of {w.m_valid} valid rows; "
                           f"fp64 MX dequantize + matmul), {dt:.2f} s; quantization untimed"}
-    if w.op == "mx":
-        qa, sa = o.quantize_mx_1x32(x["a"])
-        qb, sb = o.quantize_mx_1x32(x["b"])
+    if w.op in ("mx", "mx4"):
+        qa, sa = quant_mx(x["a"])
+        qb, sb = quant_mx(x["b"])
         t0 = time.perf_counter()
-        o.grouped_gemm_mx_contiguous(qa, sa, qb, sb, x["grouped_layout"])
+        gemm_mx(qa, sa, qb, sb, x["grouped_layout"])
         dt = time.perf_counter() - t0
         return {"value": round(w.flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                 "sample": f"one full step of {w.name} (fp64 MX dequantize + matmul over all valid rows), "
@@ -321,16 +327,16 @@ def main():
         x = wl.draw(w, seed_offset=s)
         if s == 0:
             x0 = x
-        mx = w.op == "mx"
+        mxq = {"mx": gfg.fp8_quantize_mx_1x32, "mx4": gfg.fp4_quantize_mx_1x32}.get(w.op)
         if w.layout == "masked":
-            qa, sa = gfg.fp8_quantize_mx_1x32(x["a"]) if mx else gfg.fp8_quantize_act_masked(x["a"])
+            qa, sa = mxq(x["a"]) if mxq else gfg.fp8_quantize_act_masked(x["a"])
             meta = torch.from_numpy(np.asarray(w.masked_m, np.int32)).to(dev)
             M_rows = w.G * w.M_max
         else:
-            qa, sa = gfg.fp8_quantize_mx_1x32(x["a"]) if mx else gfg.fp8_quantize_act_1x128(x["a"])
+            qa, sa = mxq(x["a"]) if mxq else gfg.fp8_quantize_act_1x128(x["a"])
             meta = torch.from_numpy(x["grouped_layout"]).to(dev)
             M_rows = w.M
-        qb, sb = gfg.fp8_quantize_mx_1x32(x["b"]) if mx else gfg.fp8_quantize_weight_128x128(x["b"])
+        qb, sb = mxq(x["b"]) if mxq else gfg.fp8_quantize_weight_128x128(x["b"])
         b_dev, sb_dev = torch.from_numpy(qb).to(dev), torch.from_numpy(sb).to(dev)
         if w.b_distinct:      # every expert its own copy in device memory
             idx = torch.from_numpy(x["b_index"]).to(dev)
@@ -353,7 +359,8 @@ def main():
         silu = w.op == "silu_mul"
         n_arg = w.I if silu else w.N      # the silu_mul entry points take I (B has 2*I rows)
         fns = {"gemm": (gfg.raw_contiguous, gfg.raw_masked), "silu_mul": (gfg.raw_silu_mul_contiguous,
-               gfg.raw_silu_mul_masked), "mx": (gfg.raw_mx_contiguous, gfg.raw_mx_masked)}[w.op]
+               gfg.raw_silu_mul_masked), "mx": (gfg.raw_mx_contiguous, gfg.raw_mx_masked),
+               "mx4": (gfg.raw_mx4_contiguous, gfg.raw_mx4_masked)}[w.op]
         if w.layout == "masked":
             a = (t["a"].data_ptr(), t["sa"].data_ptr(), t["b"].data_ptr(), t["sb"].data_ptr(),
                  t["meta"].data_ptr(), t["d"].data_ptr(), w.G, w.M_max, n_arg, w.K, out_code, handle)
@@ -385,9 +392,10 @@ def main():
     traffic = traffic_from_profile(w)
     abytes = algorithmic_bytes(w)
     gbps = abytes / (ms * 1e-3) / 1e9
-    if w.flops / abytes >= RIDGE_FLOP_PER_BYTE:
-        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP8_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+    peak = PEAK_FP4_TFLOPS if w.op == "mx4" else PEAK_FP8_TFLOPS
+    if w.flops / abytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
     else:   # below the ridge the algorithmic bytes bound the step
         roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": traffic}
@@ -403,12 +411,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3",
+        "dtype": "fp4e2m1" if w.op == "mx4" else "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "op": w.op, "layout": w.layout, "G": w.G, "N": w.N, "K": w.K,
                    "M_rows": w.M, "M_valid": w.m_valid, "out": w.out_dtype,
                    "input_sets": nsets, "parallelism": "none (1 GPU)"},
         "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
+        "pct_of_mfma_peak_for_dtype": round(100.0 * tflops / peak, 2),
         "roofline": roofline,
         "algorithmic_bytes_per_step": abytes,
         "algorithmic_GBps": round(gbps, 1),

@@ -31,6 +31,8 @@ __all__ = [
     "raw_silu_mul_contiguous", "raw_silu_mul_masked",
     "grouped_mxfp8_gemm_contiguous", "grouped_mxfp8_gemm_masked", "fp8_quantize_mx_1x32",
     "raw_mx_contiguous", "raw_mx_masked",
+    "grouped_mxfp4_gemm_contiguous", "grouped_mxfp4_gemm_masked", "fp4_quantize_mx_1x32",
+    "raw_mx4_contiguous", "raw_mx4_masked",
     "OUT_BF16", "OUT_F16", "IN_F32", "IN_BF16",
 ]
 
@@ -70,6 +72,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.grouped_mxfp8_gemm_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
     lib.grouped_mxfp8_gemm_masked.restype = ctypes.c_int
     lib.fp8_quantize_mx_1x32.argtypes = [vp, i32, i64, i64, vp, vp]
+    lib.grouped_mxfp4_gemm_contiguous.argtypes = [vp, u8p, vp, u8p, vp, vp, i64, i64, i64, i32, i32, vp]
+    lib.grouped_mxfp4_gemm_contiguous.restype = ctypes.c_int
+    lib.grouped_mxfp4_gemm_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
+    lib.grouped_mxfp4_gemm_masked.restype = ctypes.c_int
+    lib.fp4_quantize_mx_1x32.argtypes = [vp, i32, i64, i64, vp, vp]
+    lib.fp4_quantize_mx_1x32.restype = ctypes.c_int
     lib.fp8_quantize_mx_1x32.restype = ctypes.c_int
     lib.fp8_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp]
     lib.fp8_quantize_act_1x128.restype = ctypes.c_int
@@ -120,6 +128,17 @@ def raw_mx_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out
 
 def raw_mx_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, stream=0) -> int:
     return load_library().grouped_mxfp8_gemm_masked(a, a_scale, b, b_scale, masked_m, d,
+                                                    G, M_max, N, K, out_dtype, stream)
+
+
+def raw_mx4_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out_dtype, stream=0) -> int:
+    """K counts E2M1 elements (rows are K/2 bytes)."""
+    return load_library().grouped_mxfp4_gemm_contiguous(a, a_scale, b, b_scale, grouped_layout, d,
+                                                        M, N, K, G, out_dtype, stream)
+
+
+def raw_mx4_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, stream=0) -> int:
+    return load_library().grouped_mxfp4_gemm_masked(a, a_scale, b, b_scale, masked_m, d,
                                                     G, M_max, N, K, out_dtype, stream)
 
 
@@ -377,3 +396,58 @@ def fp8_quantize_mx_1x32(x):
     s = np.empty((G, K // 32, R), np.uint8)
     _check(load_library().fp8_quantize_mx_1x32(x3.ctypes.data, G, R, K, q.ctypes.data, s.ctypes.data))
     return (q[0], s[0]) if squeeze else (q, s)
+
+
+def fp4_quantize_mx_1x32(x):
+    """MXFP4 quantization on the host: x [R, K] or [G, R, K] float32 (K a multiple
+    of 128) -> (q [..., R, K/2] uint8, two E2M1 codes per byte, low nibble first;
+    scale_t [..., K/32, R])."""
+    x = _host_f32(x, "x")
+    squeeze = x.ndim == 2
+    x3 = x[None] if squeeze else x
+    G, R, K = x3.shape
+    q = np.empty((G, R, K // 2), np.uint8)
+    s = np.empty((G, K // 32, R), np.uint8)
+    _check(load_library().fp4_quantize_mx_1x32(x3.ctypes.data, G, R, K, q.ctypes.data, s.ctypes.data))
+    return (q[0], s[0]) if squeeze else (q, s)
+
+
+def grouped_mxfp4_gemm_contiguous(a, a_scale, b, b_scale, grouped_layout, d, stream=None):
+    """MXFP4 contiguous grouped GEMM: a [M, K/2] uint8 (E2M1 pairs, low nibble first), a_scale
+    [K/32, M], b [G, N, K/2], b_scale [G, K/32, N], d [M, N]."""
+    torch = _torch()
+    dev = d.device
+    M, Kh = a.shape
+    G, N, Kb = b.shape
+    K = 2 * Kh
+    if Kb != Kh or tuple(d.shape) != (M, N) or tuple(grouped_layout.shape) != (M,):
+        raise ValueError("shape mismatch between a, b, grouped_layout and d")
+    if tuple(a_scale.shape) != (K // 32, M) or tuple(b_scale.shape) != (G, K // 32, N):
+        raise ValueError("scale tensor shapes do not match the MX (1,32) layouts")
+    u8 = (torch.uint8,)
+    _check(raw_mx4_contiguous(
+        _dev_ptr(a, "a", u8, dev), _dev_ptr(a_scale, "a_scale", u8, dev), _dev_ptr(b, "b", u8, dev),
+        _dev_ptr(b_scale, "b_scale", u8, dev), _dev_ptr(grouped_layout, "grouped_layout", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev), M, N, K, G, _out_code(d), _stream_handle(stream, dev)))
+    return d
+
+
+def grouped_mxfp4_gemm_masked(a, a_scale, b, b_scale, masked_m, d, stream=None):
+    """MXFP4 masked grouped GEMM: a [G, M_max, K/2], a_scale [G, K/32, M_max], b [G, N, K/2],
+    b_scale [G, K/32, N], masked_m [G] int32 (device), d [G, M_max, N]."""
+    torch = _torch()
+    dev = d.device
+    G, Mmax, Kh = a.shape
+    Gb, N, Kb = b.shape
+    K = 2 * Kh
+    if Gb != G or Kb != Kh or tuple(d.shape) != (G, Mmax, N) or tuple(masked_m.shape) != (G,):
+        raise ValueError("shape mismatch between a, b, masked_m and d")
+    if tuple(a_scale.shape) != (G, K // 32, Mmax) or tuple(b_scale.shape) != (G, K // 32, N):
+        raise ValueError("scale tensor shapes do not match the MX (1,32) layouts")
+    u8 = (torch.uint8,)
+    _check(raw_mx4_masked(
+        _dev_ptr(a, "a", u8, dev), _dev_ptr(a_scale, "a_scale", u8, dev), _dev_ptr(b, "b", u8, dev),
+        _dev_ptr(b_scale, "b_scale", u8, dev), _dev_ptr(masked_m, "masked_m", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev), G, Mmax, N, K, _out_code(d),
+        _stream_handle(stream, dev)))
+    return d

@@ -135,7 +135,7 @@ __device__ __forceinline__ int scale_byte(int word, const uint8_t* row, int kb) 
 // Per-tile, per-lane constants of the K loop.  SAW: the lane's four A-scale
 // bytes (rows 4*l16 .. 4*l16+3 of its wave's 64) are read as one aligned dword
 // (scale rows a multiple of 4 bytes apart); otherwise as four bytes.
-template <int BN_, bool SAW_, bool SILU_ = false, bool MX_ = false>
+template <int BN_, bool SAW_, bool SILU_ = false, bool MX_ = false, bool MX4_ = false>
 struct TileCtx {
     static constexpr int BN = BN_;
     static constexpr bool SAW = SAW_;
@@ -148,7 +148,15 @@ struct TileCtx {
     // one dword per lane and operand, bytes y (A) or x (B) picked by op_sel,
     // and B is staged like A (fragment rows 4*l16 + x) so that a lane's four B
     // rows are adjacent in the transposed scale layout.
-    static constexpr bool MX = MX_;
+    static constexpr bool MX = MX_ || MX4_;
+    // MXFP4: E2M1 elements two per byte, so a 128-byte stage row holds 256 K
+    // values and feeds two scaled MFMAs, on the lane's 16-byte chunks lq and
+    // lq + 4, with a scale dword per half and operand: sa[0], sa[1] for A; sb
+    // and sbu for B.  For E2M1 the MFMA takes a lane's 16 bytes as 32
+    // consecutive K values, one scale block, and applies lane group b's scale
+    // to K [32b, 32b + 32) (measured with a one-hot probe), so the plain
+    // packing (element 2i in the low nibble of byte i) is its operand order.
+    static constexpr bool MX4 = MX4_;
     // gemm1 with silu_mul: the B tile holds gate and up rows, and fragments
     // x < FN/2 (gate) take the gate block's scale, x >= FN/2 (up) the up block's
     static constexpr bool SILU = SILU_;
@@ -162,7 +170,7 @@ struct TileCtx {
     // vector-memory loads one wave issues per stage: DMAs and the A scales (one
     // dword or FM bytes); the B-scale dword is a scalar load
     static constexpr int SA_LOADS = SAW ? 1 : FM;
-    static constexpr int LOADS = A_DMA + B_DMA + SA_LOADS + (MX ? 1 : 0);   // MX: + the B-scale dword
+    static constexpr int LOADS = A_DMA + B_DMA + SA_LOADS + (MX ? 1 : 0) + (MX4 ? 2 : 0);   // + B-scale dwords
 
     // Buffer resources (scalar registers): base + byte count.  The hardware
     // returns zero for any offset past the count instead of touching memory.
@@ -174,6 +182,7 @@ struct TileCtx {
     uint32_t sa_stride;        // scale_a bytes between 128-wide K steps
     __amdgpu_buffer_rsrc_t sb_rsrc;   // MX: scale_b of expert g from column n0 of block 0
     uint32_t sb_off, sb_stride;       // MX: this lane's B-scale dword offset, bytes per K step
+    uint32_t sb_off1;                 // MX4: the second half's B-scale dword offset (sa_off[1]: A's)
     uint32_t a_off[A_DMA];     // per-lane source offsets of this wave's DMA chunks
     uint32_t b_off[B_DMA];
     uint32_t sa_off[4];        // A-scale byte offsets (SAW: [0] only, the dword)
@@ -221,6 +230,10 @@ __device__ __forceinline__ void issue_stage(const C& c, GFG_LDS uint8_t* __restr
     else
         sb = load_scale_word(c.sb_row, kb);
     if constexpr (C::SILU) sbu = load_scale_word(c.sbu_row, kb);
+    if constexpr (C::MX4) {
+        sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(c.sa_rsrc, c.sa_off[1], uint32_t(kb) * c.sa_stride, 0));
+        sbu = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off1, uint32_t(kb) * c.sb_stride, 0));
+    }
     // K-block base pointers made opaque scalars, so each DMA address is a scalar
     // base plus this lane's 32-bit offset (no per-lane 64-bit induction variables)
     const uint8_t* ak = uniform_ptr(c.a_tile + int64_t(kb) * BK);
@@ -268,22 +281,35 @@ __device__ __forceinline__ void read_frags(const C& c, const GFG_LDS uint8_t* __
 // MFMAs of A fragment Y against every B fragment: the A scale is byte Y of
 // the packed word (op_sel picks it), the B scale the wave's byte.
 // (MX: the B scale is byte X of the lane's dword, the scale of its row 4*l16 + X.)
+// (MX4: two FP4 MFMAs per fragment pair, on the low and the high 16 bytes of
+// the lane's fragments; saw/sb scale the first, saw1/sbu the second.)
 template <class C, int Y, int X = 0>
-__device__ __forceinline__ void mfma_row(const Frags<C::BN>& f, int saw, int sb, int sbu, v4f (&acc)[C::FN][4]) {
+__device__ __forceinline__ void mfma_row(const Frags<C::BN>& f, int saw, int sb, int sbu, int saw1,
+                                         v4f (&acc)[C::FN][4]) {
     if constexpr (X < C::FN) {
-        acc[X][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            f.b[X], f.a[Y], acc[X][Y], 0, 0, C::MX ? X : 0, (C::SILU && X >= C::FN / 2) ? sbu : sb, Y, saw);
-        mfma_row<C, Y, X + 1>(f, saw, sb, sbu, acc);
+        if constexpr (C::MX4) {
+            acc[X][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[X], f.a[Y], acc[X][Y], 4, 4, X, sb, Y,
+                                                                         saw);
+            acc[X][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                __builtin_shufflevector(f.b[X], f.b[X], 4, 5, 6, 7, -1, -1, -1, -1),
+                __builtin_shufflevector(f.a[Y], f.a[Y], 4, 5, 6, 7, -1, -1, -1, -1), acc[X][Y], 4, 4, X, sbu, Y,
+                saw1);
+        } else {
+            acc[X][Y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                f.b[X], f.a[Y], acc[X][Y], 0, 0, C::MX ? X : 0, (C::SILU && X >= C::FN / 2) ? sbu : sb, Y, saw);
+        }
+        mfma_row<C, Y, X + 1>(f, saw, sb, sbu, saw1, acc);
     }
 }
 
 template <class C>
-__device__ __forceinline__ void mfma_stage(const Frags<C::BN>& f, int saw, int sb, int sbu, v4f (&acc)[C::FN][4]) {
+__device__ __forceinline__ void mfma_stage(const Frags<C::BN>& f, int saw, int sb, int sbu, int saw1,
+                                           v4f (&acc)[C::FN][4]) {
     static_assert(C::FM == 4, "four A fragments per wave");
-    mfma_row<C, 0>(f, saw, sb, sbu, acc);
-    mfma_row<C, 1>(f, saw, sb, sbu, acc);
-    mfma_row<C, 2>(f, saw, sb, sbu, acc);
-    mfma_row<C, 3>(f, saw, sb, sbu, acc);
+    mfma_row<C, 0>(f, saw, sb, sbu, saw1, acc);
+    mfma_row<C, 1>(f, saw, sb, sbu, saw1, acc);
+    mfma_row<C, 2>(f, saw, sb, sbu, saw1, acc);
+    mfma_row<C, 3>(f, saw, sb, sbu, saw1, acc);
 }
 
 // One K-step k.  On entry: fragments of stage k are in `cur` (their LDS reads
@@ -321,7 +347,8 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
     __builtin_amdgcn_sched_barrier(0);
     const int sa_use = sa_word<C>(sa);
     const int sb_use = C::MX ? sb : scale_byte(sb, c.sb_row, kb_cur);
-    const int sbu_use = C::SILU ? scale_byte(sbu, c.sbu_row, kb_cur) : sb_use;
+    const int sbu_use = C::MX4 ? sbu : (C::SILU ? scale_byte(sbu, c.sbu_row, kb_cur) : sb_use);
+    const int saw1 = C::MX4 ? sa[1] : 0;
     // The LDS DMA and the fragment reads are issued here, through this
     // function's restrict parameters, so the compiler knows the refilled
     // buffer and the buffer being read do not overlap and adds no wait for
@@ -353,7 +380,7 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
             nxt.b[x] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     }
-    mfma_stage<C>(cur, sa_use, sb_use, sbu_use, acc);
+    mfma_stage<C>(cur, sa_use, sb_use, sbu_use, saw1, acc);
     if (ISSUE) {   // after the MFMAs that read the old scale registers
         load_sa(c, kb_refill, sa);
         if constexpr (C::MX)
@@ -361,9 +388,15 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
         else
             sb = load_scale_word(c.sb_row, kb_refill);
         if constexpr (C::SILU) sbu = load_scale_word(c.sbu_row, kb_refill);
+        if constexpr (C::MX4) {
+            sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(c.sa_rsrc, c.sa_off[1], uint32_t(kb_refill) * c.sa_stride,
+                                                             0));
+            sbu = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off1, uint32_t(kb_refill) * c.sb_stride,
+                                                           0));
+        }
     }
-    sched_pattern<0, C::FN * C::FM, ISSUE ? C::A_DMA + C::B_DMA : 0, READ ? 2 * (C::FM + C::FN) : 0,
-                  ISSUE ? C::SA_LOADS + (C::MX ? 1 : 0) : 0>();
+    sched_pattern<0, C::FN * C::FM * (C::MX4 ? 2 : 1), ISSUE ? C::A_DMA + C::B_DMA : 0,
+                  READ ? 2 * (C::FM + C::FN) : 0, ISSUE ? C::LOADS - C::A_DMA - C::B_DMA : 0>();
     if (READ) cur = nxt;
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -388,11 +421,12 @@ __device__ __forceinline__ v4f silu_mul4(v4f gv, v4f uv) {
 // as its 256 B rows, interleaved so that each wave's 64 columns are 32 gate
 // and the same 32 up columns: fragments x and x + FN/2 of a lane then hold the
 // gate and up values of the same four outputs.
-template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU, bool MX>
+// (MX4: p.K counts bytes of a row, half its E2M1 elements.)
+template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU, bool MX, bool MX4 = false>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p) {
     static_assert(!SILU || BN == 256, "the gate/up interleave assumes 64 B rows per wave");
-    static_assert(!MX || (BN == 256 && SAW && !SILU), "MX runs on the 256-column tile with packed scale words");
-    using C = TileCtx<BN, SAW, SILU, MX>;
+    static_assert(!(MX || MX4) || (BN == 256 && SAW && !SILU), "MX runs on the 256-column tile with packed scale words");
+    using C = TileCtx<BN, SAW, SILU, MX, MX4>;
     constexpr int FN = C::FN, FM = C::FM, WN = C::WN;
     constexpr int L = C::LOADS;
 
@@ -451,7 +485,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
     const int KB = p.K / BK;
     const int NB = p.N / 128;
     const int n_out = SILU ? p.N / 2 : p.N;   // output row length
-    const int SKB = MX ? 4 * KB : KB;           // scale blocks along K (MX: 32 wide)
+    const int SKB = (MX4 ? 8 : MX ? 4 : 1) * KB;   // scale blocks along K (MX: 32 elements wide)
     const int wm = wave & 1, wn = wave >> 1;
     const int l16 = lane & 15, lq = lane >> 4;
     GFG_LDS uint8_t* const buf0 = (GFG_LDS uint8_t*)smem0;
@@ -500,20 +534,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         c.a_tile = a_reg + m0 * p.K;
         c.b_tile = p.b + (int64_t(g) * p.N + n0) * p.K;
         c.sa_rsrc = make_rsrc(sa_reg + m0, uint32_t(int64_t(SKB) * p.rows - m0));
-        if constexpr (MX) {
+        if constexpr (C::MX) {
             // scale_b [G][K/32][N]: this lane's dword holds rows n0 + wn*WN +
-            // 4*l16 .. +3 of block 4*kb + lq
+            // 4*l16 .. +3 of block 4*kb + lq (MX4: 8*kb + lq, and 8*kb + 4 + lq)
             const int64_t sbe = int64_t(g) * SKB * p.N;
             c.sb_rsrc = make_rsrc(p.b_scale + sbe + n0, uint32_t(int64_t(SKB) * p.N - n0));
             c.sb_off = uint32_t(lq * p.N + wn * WN + 4 * l16);
-            c.sb_stride = uint32_t(4 * p.N);
+            c.sb_off1 = c.sb_off + uint32_t(4 * p.N);
+            c.sb_stride = uint32_t((MX4 ? 8 : 4) * p.N);
         } else if constexpr (SILU) {
             c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + n0 / 128) * KB);
             c.sbu_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n_out + n0) / 128) * KB);
         } else {
             c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB);
         }
-        c.sa_stride = uint32_t(MX ? 4 * p.rows : p.rows);
+        c.sa_stride = uint32_t((MX4 ? 8 : MX ? 4 : 1) * p.rows);
         // DMA chunk j of this wave fills LDS rows 8*(j*WAVES + wave) .. +7; lane i
         // writes physical chunk i%8 of tile row R = +i/8, which holds logical
         // chunk (i%8) ^ key(R) of that row (A: key (R >> 2) & 7, B: R & 7).
@@ -533,7 +568,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
                 // SILU: LDS rows 64w .. 64w+31 hold gate rows o0 + 32w .., rows
                 // 64w+32 .. 64w+63 the up rows I + o0 + 32w .. (B rows from n0)
                 const int w = R >> 6, q = R & 63;
-                if constexpr (MX) {   // staged like A: row a_row(R), key (R >> 2) & 7
+                if constexpr (C::MX) {   // staged like A: row a_row(R), key (R >> 2) & 7
                     c.b_off[j] = uint32_t(a_row(R)) * uint32_t(p.K) + uint32_t((pc ^ ((R >> 2) & 7)) * 16);
                 } else {
                     const int brow = !SILU ? R : (q < 32 ? 32 * w + q : n_out + 32 * w + (q - 32));
@@ -547,7 +582,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         // the buffer read returns 0 (such rows are never stored).
         if constexpr (SAW) {
             // (MX: block 4*kb + lq of the lane's 32-wide K chunk)
-            c.sa_off[0] = uint32_t((MX ? lq * int(p.rows) : 0) + wm * 64 + 4 * l16);
+            c.sa_off[0] = uint32_t((C::MX ? lq * int(p.rows) : 0) + wm * 64 + 4 * l16);
+            if constexpr (MX4) c.sa_off[1] = c.sa_off[0] + uint32_t(4 * p.rows);
         } else {
 #pragma unroll
             for (int f = 0; f < FM; ++f) {
@@ -630,7 +666,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             const int row = int(m0) + wm * 64 + 4 * l16 + y;   // rows of a region fit in 32 bits
             const bool ok = row < mlimit && (MASKED || int(lay[y]) == g);
             if (!ok) continue;
-            if constexpr (MX) {
+            if constexpr (C::MX) {
                 // lane holds columns wn*WN + 16lq + 4i + x: value acc[x][y][i]
                 typedef OutT out8 __attribute__((ext_vector_type(8)));
                 OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * p.N + n0 + wn * WN + 16 * lq;
@@ -682,7 +718,7 @@ int device_info(DeviceInfo* out) {
     return GFG_OK;
 }
 
-template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU = false, bool MX = false>
+template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU = false, bool MX = false, bool MX4 = false>
 int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     DeviceInfo di;
     if (int rc = device_info(&di)) return rc;
@@ -691,8 +727,8 @@ int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     unsigned grid = upper < unsigned(di.cus) ? upper : unsigned(di.cus);
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;          // whole slots on every XCD
     if (grid == 0) return GFG_OK;
-    hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, SAW, OutT, SILU, MX>), dim3(grid), dim3(NTHREADS), 0, s,
-                       p);
+    hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, SAW, OutT, SILU, MX, MX4>), dim3(grid), dim3(NTHREADS), 0,
+                       s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(GFG_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return GFG_OK;
@@ -812,10 +848,10 @@ int check_mx(const char* fn, int64_t N, int64_t rows, const uint8_t* a_scale, co
     return GFG_OK;
 }
 
-template <bool MASKED>
+template <bool MASKED, bool MX4 = false>
 int dispatch_mx(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
-    return out_dtype == GFG_OUT_BF16 ? launch_t<256, MASKED, true, __bf16, false, true>(p, n_cand, s)
-                                     : launch_t<256, MASKED, true, _Float16, false, true>(p, n_cand, s);
+    return out_dtype == GFG_OUT_BF16 ? launch_t<256, MASKED, true, __bf16, false, !MX4, MX4>(p, n_cand, s)
+                                     : launch_t<256, MASKED, true, _Float16, false, !MX4, MX4>(p, n_cand, s);
 }
 
 template <bool MASKED>
@@ -913,4 +949,44 @@ extern "C" int grouped_mxfp8_gemm_masked(const void* a, const uint8_t* a_scale, 
     if (int rc = check_mx(fn, N, M_max, a_scale, b_scale)) return rc;
     if (M_max == 0) return GFG_OK;
     return dispatch_mx<true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
+}
+
+// MXFP4: K counts E2M1 elements; the rows of a and b are K/2 bytes.  K must be
+// a multiple of 256 (one 128-byte stage), checked here before the byte sizes
+// go to the common checks.
+static int check_k4(const char* fn, int64_t K) {
+    if (K <= 0) return fail(GFG_EINVAL, "%s: K=%lld must be positive", fn, (long long)K);
+    if (K % 256) return fail(GFG_EUNSUPPORTED, "%s: K=%lld must be a multiple of 256", fn, (long long)K);
+    return GFG_OK;
+}
+
+extern "C" int grouped_mxfp4_gemm_contiguous(const void* a, const uint8_t* a_scale, const void* b,
+                                             const uint8_t* b_scale, const int32_t* grouped_layout, void* d,
+                                             int64_t M, int64_t N, int64_t K, int32_t G, int32_t out_dtype,
+                                             void* stream) {
+    clear_error();
+    const char* fn = "grouped_mxfp4_gemm_contiguous";
+    if (int rc = check_k4(fn, K)) return rc;
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, N, K / 2, G, out_dtype, &p, &n_cand))
+        return rc;
+    if (int rc = check_mx(fn, N, M, a_scale, b_scale)) return rc;
+    if (M == 0) return GFG_OK;
+    return dispatch_mx<false, true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int grouped_mxfp4_gemm_masked(const void* a, const uint8_t* a_scale, const void* b,
+                                         const uint8_t* b_scale, const int32_t* masked_m, void* d, int32_t G,
+                                         int64_t M_max, int64_t N, int64_t K, int32_t out_dtype, void* stream) {
+    clear_error();
+    const char* fn = "grouped_mxfp4_gemm_masked";
+    if (int rc = check_k4(fn, K)) return rc;
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K / 2, out_dtype, &p, &n_cand))
+        return rc;
+    if (int rc = check_mx(fn, N, M_max, a_scale, b_scale)) return rc;
+    if (M_max == 0) return GFG_OK;
+    return dispatch_mx<true, true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
 }

@@ -76,6 +76,38 @@ bool mx_floor_e8m0(float amax, int* t) {
     return true;
 }
 
+// MXFP4 scale exponent: t = floor(log2(amax)) - 2 (E2M1's largest power of two
+// is 4), so the scaled block's largest magnitude lies in [4, 8); values above
+// 6 saturate.
+bool mx4_floor_e8m0(float amax, int* t) {
+    if (!(amax >= 0.0f) || std::isinf(amax)) return false;
+    if (amax == 0.0f) { *t = 0; return true; }
+    int p;
+    std::frexp(amax, &p);
+    const int tt = p - 1 - 2;
+    if (tt < -127 || tt > 127) return false;
+    *t = tt;
+    return true;
+}
+
+// Nearest E2M1 code of v (|v| <= 6): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 are
+// codes 0..7; a value on a midpoint takes the code with an even mantissa bit
+// (so 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0,
+// 5 -> 4.0).  Bit 3 is the sign, kept for zero.
+inline uint8_t e2m1_rne(float v) {
+    const float a = std::fabs(v);
+    uint8_t c;
+    if (a <= 0.25f) c = 0;
+    else if (a < 0.75f) c = 1;
+    else if (a <= 1.25f) c = 2;
+    else if (a < 1.75f) c = 3;
+    else if (a <= 2.5f) c = 4;
+    else if (a < 3.5f) c = 5;
+    else if (a <= 5.0f) c = 6;
+    else c = 7;
+    return uint8_t(c | (std::signbit(v) ? 8 : 0));
+}
+
 // Nearest E4M3FN code of v (|v| <= 448), ties to the even mantissa.
 inline uint8_t e4m3_rne(float v) {
     uint32_t u = f2u(v);
@@ -212,6 +244,50 @@ extern "C" int fp8_quantize_mx_1x32(const float* x, int32_t G, int64_t R, int64_
                 const float v = std::ldexp(row[k], -t);
                 q[gr * K + k] = e4m3_rne(std::min(448.0f, std::max(-448.0f, v)));
             }
+        }
+    });
+    for (int64_t i = 0; i < int64_t(G) * R; ++i)
+        if (bad[size_t(i)])
+            return fail(GFG_ERANGE, "%s: row %lld has a block outside the E8M0 range or a non-finite value", fn,
+                        (long long)i);
+    return GFG_OK;
+}
+
+extern "C" int fp4_quantize_mx_1x32(const float* x, int32_t G, int64_t R, int64_t K, uint8_t* q,
+                                    uint8_t* scale_t) {
+    clear_error();
+    const char* fn = "fp4_quantize_mx_1x32";
+    if (G <= 0 || R < 0 || K <= 0)
+        return fail(GFG_EINVAL, "%s: bad sizes G=%d R=%lld K=%lld", fn, G, (long long)R, (long long)K);
+    if (K % 128) return fail(GFG_EUNSUPPORTED, "%s: K=%lld must be a multiple of 128", fn, (long long)K);
+    if (R == 0) return GFG_OK;
+    if (!x || !q || !scale_t) return fail(GFG_EINVAL, "%s: null pointer", fn);
+    const int64_t KB = K / 32;
+    std::vector<int> bad(size_t(G * R), 0);
+    parallel_for(int64_t(G) * R, [&](int64_t gr) {
+        const int64_t g = gr / R, r = gr % R;
+        const float* row = x + gr * K;
+        uint8_t codes[128];
+        for (int64_t q0 = 0; q0 < K; q0 += 128) {          // one 128-element group, 64 bytes out
+            for (int j = 0; j < 4; ++j) {
+                const int64_t k0 = q0 + 32 * j;
+                float amax = 0.0f;
+                bool nan = false;
+                for (int i = 0; i < 32; ++i) {
+                    amax = std::max(amax, std::fabs(row[k0 + i]));
+                    nan |= row[k0 + i] != row[k0 + i];
+                }
+                int t;
+                if (nan || !mx4_floor_e8m0(amax, &t)) { bad[size_t(gr)] = 1; return; }
+                scale_t[(g * KB + k0 / 32) * R + r] = uint8_t(t + 127);
+                for (int i = 0; i < 32; ++i) {
+                    const float v = std::ldexp(row[k0 + i], -t);
+                    codes[32 * j + i] = e2m1_rne(std::min(6.0f, std::max(-6.0f, v)));
+                }
+            }
+            // two elements per byte, the lower index in the low nibble
+            uint8_t* out = q + gr * (K / 2) + q0 / 2;
+            for (int j = 0; j < 64; ++j) out[j] = uint8_t(codes[2 * j] | (codes[2 * j + 1] << 4));
         }
     });
     for (int64_t i = 0; i < int64_t(G) * R; ++i)

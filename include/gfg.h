@@ -177,6 +177,44 @@ GFG_API int fp8_quantize_mx_1x32(const float* x, int32_t G, int64_t R, int64_t K
                          uint8_t* q, uint8_t* scale_t);
 
 /*
+ * MXFP4 grouped GEMM: the two layouts on E2M1 operands (the "mxfp4 (a4w4)"
+ * element type of the third reference page, "flydsl mxfp4 a4w4 MoE: bring
+ * gemm1/gemm2 to parity with the HIP backend", section "Summary"), one E8M0
+ * scale per 32 K elements of every row, as in the MXFP8 GEMM.  K counts E2M1
+ * elements; each row of a and b is K/2 bytes, two elements per byte with
+ * the lower K index in the low nibble (as fp4_quantize_mx_1x32 writes).
+ *
+ *   a         contiguous [M][K/2], masked [G][M_max][K/2]      E2M1, two per byte
+ *   b         [G][N][K/2]
+ *   a_scale   contiguous [K/32][M], masked [G][K/32][M_max]
+ *   b_scale   [G][K/32][N]
+ *
+ * Sizes: as the MXFP8 GEMM, with K a multiple of 256 (else GFG_EUNSUPPORTED).
+ */
+GFG_API int grouped_mxfp4_gemm_contiguous(const void* a, const uint8_t* a_scale,
+                                  const void* b, const uint8_t* b_scale,
+                                  const int32_t* grouped_layout, void* d,
+                                  int64_t M, int64_t N, int64_t K, int32_t G,
+                                  int32_t out_dtype, void* stream);
+GFG_API int grouped_mxfp4_gemm_masked(const void* a, const uint8_t* a_scale,
+                              const void* b, const uint8_t* b_scale,
+                              const int32_t* masked_m, void* d,
+                              int32_t G, int64_t M_max, int64_t N, int64_t K,
+                              int32_t out_dtype, void* stream);
+
+/*
+ * MXFP4 quantizer (CPU, synchronous):
+ *   x [G][R][K] float -> q [G][R][K/2] (two E2M1 codes per byte), scale_t [G][K/32][R] E8M0.
+ * Per row and 32-wide K block: t = floor(log2(max|x|)) - 2 (t = 0 for an
+ * all-zero block), scale byte t + 127, code = E2M1(clamp(x / 2^t, -6, 6))
+ * nearest-even (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 the sign).
+ * Byte i of a row holds elements 2i (low nibble) and 2i + 1.  K must be a
+ * multiple of 128 (else GFG_EUNSUPPORTED); GFG_ERANGE as fp8_quantize_mx_1x32.
+ */
+GFG_API int fp4_quantize_mx_1x32(const float* x, int32_t G, int64_t R, int64_t K,
+                         uint8_t* q, uint8_t* scale_t);
+
+/*
  * Host quantizers (CPU, synchronous), ceil-E8M0 scales and nearest-even E4M3:
  * for each block, t = the smallest integer with 448 * 2^t >= amax (t = 0 for
  * an all-zero block), scale byte = t + 127, q = E4M3(x / 2^t).  The rounding

@@ -283,3 +283,69 @@ def test_mx_gemm_argument_errors(fn):
     assert fn(**rows) == 2
     empty = {"M": 0} if fn is _mc else {"Mmax": 0}
     assert fn(**empty) == 0
+
+
+# ------------------------------------------------------------------ MXFP4
+@pytest.mark.parametrize("shape", [(1, 128), (7, 256), (3, 40, 384)])
+def test_mx4_quantizer_bit_exact(shape):
+    rng = np.random.default_rng(sum(shape) + 4)
+    x = (rng.standard_normal(shape) * 10.0 ** rng.uniform(-4, 4, shape[:-1] + (1,))).astype(np.float32)
+    q, s = gfg.fp4_quantize_mx_1x32(x)
+    oq, os_ = o.quantize_mx4_1x32(x)
+    assert np.array_equal(q, oq) and np.array_equal(s, os_)
+
+
+def test_mx4_quantizer_boundaries_bit_exact():
+    """Exponent edges (amax = 4*2^t, one ulp below, 8*2^t), saturating blocks
+    (scaled maximum in (6, 8)), every E2M1 midpoint, an all-zero block and
+    negative zeros."""
+    blocks = []
+    for t in (-30, -1, 0, 5, 60):
+        for amax in (4.0 * 2.0 ** t, np.nextafter(4.0 * 2.0 ** t, 0), 7.5 * 2.0 ** t, 6.0 * 2.0 ** t):
+            b = np.linspace(-1, 1, 32) * amax
+            b[9] = amax
+            blocks.append(b)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    b = np.concatenate([mids, -mids, mids * 0.999, mids * 1.001])
+    blocks.append(b)                        # amax 6.006: t = 0, the 1.001 * 6 saturates
+    z = np.zeros(32)
+    z[5] = -0.0
+    blocks.append(z)
+    blocks.append(np.zeros(32))
+    x = np.stack(blocks).astype(np.float32).reshape(1, -1)
+    x = np.pad(x, ((0, 0), (0, (-x.shape[1]) % 128)))   # K a multiple of 128
+    q, s = gfg.fp4_quantize_mx_1x32(x)
+    oq, os_ = o.quantize_mx4_1x32(x)
+    assert np.array_equal(s, os_) and np.array_equal(q, oq)
+
+
+def test_mx4_quantizer_errors():
+    lib = gfg.load_library()
+    x = np.zeros((2, 128), np.float32)
+    q = np.empty((2, 64), np.uint8)
+    s = np.empty((4, 2), np.uint8)
+    assert lib.fp4_quantize_mx_1x32(x.ctypes.data, 1, 2, 96, q.ctypes.data, s.ctypes.data) == 2   # K % 128
+    assert lib.fp4_quantize_mx_1x32(None, 1, 2, 128, q.ctypes.data, s.ctypes.data) == 1
+    x[1, 40] = np.inf
+    assert lib.fp4_quantize_mx_1x32(x.ctypes.data, 1, 2, 128, q.ctypes.data, s.ctypes.data) == 4
+
+
+@pytest.mark.parametrize("contig", [True, False])
+def test_mx4_gemm_argument_errors(contig):
+    def call(**kw):
+        a = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, meta=FAKE, d=FAKE, M=256, N=256, K=512, G=2, dt=0)
+        a.update(kw)
+        if contig:
+            return gfg.raw_mx4_contiguous(a["a"], a["sa"], a["b"], a["sb"], a["meta"], a["d"], a["M"], a["N"], a["K"],
+                                          a["G"], a["dt"], 0)
+        return gfg.raw_mx4_masked(a["a"], a["sa"], a["b"], a["sb"], a["meta"], a["d"], a["G"], a["M"], a["N"], a["K"],
+                                  a["dt"], 0)
+    for k in ("a", "sa", "b", "sb", "meta", "d"):
+        assert call(**{k: None}) == 1, k
+    assert call(K=0) == 1
+    assert call(K=384) == 2            # K (elements) must be a multiple of 256
+    assert "multiple of 256" in gfg.load_library().gfg_last_error().decode()
+    assert call(N=384) == 2
+    assert call(M=130) == 2
+    assert call(sb=FAKE + 2) == 2
+    assert call(M=0) == 0
