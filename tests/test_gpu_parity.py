@@ -203,3 +203,84 @@ def test_masked_equals_contiguous_on_same_rows():
     for g, c in enumerate(counts):
         assert np.array_equal(dm[g, :c], dc[pos:pos + c])
         pos += -(-c // 128) * 128
+
+
+def test_contiguous_maximum_rows():
+    """The largest contiguous call the tile list takes: 4096 candidate tiles
+    (524,288 rows) over three experts, K = 128, N = 256.  Sampled rows
+    (each expert's first and last, the last tile's rows) against the oracle;
+    every padding row keeps the sentinel."""
+    rng = np.random.default_rng(71)
+    counts = [200_000, 100_001, 224_000]
+    layout = wl.contiguous_layout(counts)
+    assert layout.size <= 4096 * 128
+    layout = np.concatenate([layout, np.full(4096 * 128 - layout.size, -1, np.int32)])
+    M, K, N = layout.size, 128, 256
+    print(f"[parity] max rows M={M}", flush=True)
+    a = rng.standard_normal((M, K), dtype=np.float32)
+    a[layout < 0] = 0.0
+    b = rng.standard_normal((3, N, K), dtype=np.float32)
+    qa, sa = gfg.fp8_quantize_act_1x128(a)
+    qb, sb = gfg.fp8_quantize_weight_128x128(b)
+    d = gpu_contiguous(qa, sa, qb, sb, layout, "bf16")
+    got = d.float().cpu().numpy()
+    assert np.all(bits(d)[layout < 0] == sentinel_bits("bf16"))
+    del d
+    rows = []
+    for g in range(3):
+        idx = np.nonzero(layout == g)[0]
+        rows += [idx[0], idx[1], idx[-2], idx[-1]] + list(rng.choice(idx, 4, replace=False))
+    rows = np.array(sorted(set(rows)))
+    oqa, osa = o.quantize_act_1x128(a[rows])
+    oqb, osb = o.quantize_weight_128x128(b)
+    ref = o.grouped_gemm_contiguous(oqa, osa, oqb, osb, layout[rows])
+    check_close(got[rows], ref, "max rows")
+
+
+def test_masked_maximum_tiles():
+    """G * ceil(M_max / 128) = 4096 candidate tiles: 32 groups of 16,384 rows,
+    masked_m from 0 to M_max."""
+    rng = np.random.default_rng(72)
+    G, Mmax, K, N = 32, 16384, 128, 256
+    masked_m = rng.integers(0, Mmax, size=G, endpoint=True).astype(np.int32)
+    masked_m[0], masked_m[1], masked_m[-1] = 0, Mmax, 1
+    print(f"[parity] max masked tiles G={G} Mmax={Mmax}", flush=True)
+    a = rng.standard_normal((G, Mmax, K), dtype=np.float32)
+    b = rng.standard_normal((G, N, K), dtype=np.float32)
+    qa, sa = gfg.fp8_quantize_act_masked(a)
+    qb, sb = gfg.fp8_quantize_weight_128x128(b)
+    d = gpu_masked(qa, sa, qb, sb, masked_m, "bf16")
+    b_all = bits(d)
+    got = d.float().cpu().numpy()
+    del d
+    gots, refs = [], []
+    for g in range(G):
+        mm = int(masked_m[g])
+        assert np.all(b_all[g, mm:] == sentinel_bits("bf16")), f"group {g}: rows >= masked_m written"
+        if mm == 0:
+            continue
+        rows = np.array(sorted(set([0, mm - 1] + list(rng.integers(0, mm, 2)))))
+        oqa, osa = o.quantize_act_1x128(a[g][rows])
+        oqb, osb = o.quantize_weight_128x128(b[g:g + 1])
+        refs.append(o.grouped_gemm_contiguous(oqa, osa, oqb, osb, np.zeros(rows.size, np.int32)))
+        gots.append(got[g, rows])
+    check_close(np.concatenate(gots), np.concatenate(refs), "max masked tiles")
+
+
+def test_all_padding_and_all_masked_off_write_nothing():
+    """No valid tile at all: an all-padding contiguous layout and a masked call
+    whose masked_m are all zero (or negative) launch and leave the output untouched."""
+    rng = np.random.default_rng(73)
+    K, N = 256, 256
+    layout = np.full(384, -1, np.int32)
+    a = rng.standard_normal((384, K)).astype(np.float32)
+    b = rng.standard_normal((2, N, K)).astype(np.float32)
+    qa, sa = gfg.fp8_quantize_act_1x128(a)
+    qb, sb = gfg.fp8_quantize_weight_128x128(b)
+    d = gpu_contiguous(qa, sa, qb, sb, layout, "f16")
+    assert np.all(bits(d) == sentinel_bits("f16"))
+    am = rng.standard_normal((3, 256, K)).astype(np.float32)
+    qa, sa = gfg.fp8_quantize_act_masked(am)
+    qb, sb = gfg.fp8_quantize_weight_128x128(rng.standard_normal((3, N, K)).astype(np.float32))
+    d = gpu_masked(qa, sa, qb, sb, np.array([0, -4, 0], np.int32), "bf16")
+    assert np.all(bits(d) == sentinel_bits("bf16"))
