@@ -25,8 +25,11 @@
 //  * waves laid out 2 (M) x 4 (N), 64 x BN/4 outputs each; fragments for
 //    step k+1 are read from LDS while the MFMAs of step k run;
 //  * the MFMA's first operand is the B tile (N rows) and its second the A
-//    tile (M rows), so each lane ends up owning 4 consecutive output columns
-//    of one row, written as one 8-byte store.
+//    tile (M rows), so a lane's accumulators hold output columns of one row;
+//    on the 256-column tile, B fragment x takes the wave's columns 4*l16 + x,
+//    which hands each lane 16 consecutive columns of its row, written as two
+//    16-byte stores (4 consecutive columns and one 8-byte store per fragment
+//    on the 128-column tile and for silu_mul).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -60,7 +63,7 @@ struct Params {
     int N, K, G;
     int n_cand;              // candidate 128-row tiles: ceil(M/128) or G*ceil(Mmax/128)
     int mt_per_group;        // masked: ceil(Mmax/128)
-    int group_m;             // grouped-M width (in 128-row tiles)
+    int group_m;             // grouped-M width (in 128-row tiles) when the tiles take more than two rounds
 };
 
 // Byte offset of 16-byte chunk c (0..7) of row r inside a [rows][128 B] LDS tile.
@@ -157,6 +160,11 @@ struct TileCtx {
     // to K [32b, 32b + 32) (measured with a one-hot probe), so the plain
     // packing (element 2i in the low nibble of byte i) is its operand order.
     static constexpr bool MX4 = MX4_;
+    // B staged like A (LDS row p holds B row a_row(p)) with fragment x on the
+    // wave's columns 4*l16 + x: a lane's accumulators then cover 16
+    // consecutive output columns.  Every 256-column tile except silu_mul, whose
+    // tile interleaves gate and up rows.
+    static constexpr bool BL = MX || (!SILU_ && BN_ == 256);
     // gemm1 with silu_mul: the B tile holds gate and up rows, and fragments
     // x < FN/2 (gate) take the gate block's scale, x >= FN/2 (up) the up block's
     static constexpr bool SILU = SILU_;
@@ -189,7 +197,7 @@ struct TileCtx {
     // LDS byte offsets of this lane's fragment rows, logical chunks lq (lo) and
     // lq + 4 (hi).  A fragment y sits at a_*_e + y*BK for even y and at
     // a_*_o + y*BK for odd y (the row-parity exchange of the A layout).
-    // (MX: B rows as A's, at b_*_e / b_*_o.)
+    // (BL: B rows as A's, at b_*_e / b_*_o.)
     int a_lo_e, a_lo_o, a_hi_e, a_hi_o, b_lo, b_hi;
     int b_lo_e, b_lo_o, b_hi_e, b_hi_o;
 };
@@ -249,10 +257,10 @@ __device__ __forceinline__ void issue_stage(const C& c, GFG_LDS uint8_t* __restr
 }
 
 // LDS offset (from the B tile) of B fragment x's chunk for this lane: row
-// 16x + l16 of the wave's WN, or with MX row 4*l16 + x in the A-style layout.
+// 16x + l16 of the wave's WN, or with BL row 4*l16 + x in the A-style layout.
 template <class C>
 __device__ __forceinline__ int b_frag(const C& c, int x, bool hi) {
-    if constexpr (C::MX)
+    if constexpr (C::BL)
         return (hi ? ((x & 1) ? c.b_hi_o : c.b_hi_e) : ((x & 1) ? c.b_lo_o : c.b_lo_e)) + x * BK;
     else
         return (hi ? c.b_hi : c.b_lo) + x * 16 * BK;
@@ -493,9 +501,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
     GFG_LDS uint8_t* const buf2 = (GFG_LDS uint8_t*)smem2;
 
     for (unsigned i = slot; i < x_count; i += slots) {
-        // grouped-M order over (valid m-tile rank, n-tile)
+        // grouped-M order over (valid m-tile rank, n-tile).  When every
+        // workgroup has at most two tiles, an XCD's 32 concurrent tiles span
+        // 8 m-tiles x 4 n-tiles: on the 128 x 256 tile that streams 8*128 +
+        // 4*256 rows of K bytes into its L2 per round instead of 4*128 + 8*256
+        // (4 x 8), a fifth less.  Longer walks keep the narrower group_m.
         const unsigned t = x_start + i;
-        const unsigned gm = unsigned(p.group_m);
+        const unsigned gm = T <= 2u * gridDim.x ? 8u : unsigned(p.group_m);
         const unsigned per_group = gm * unsigned(NT);
         const unsigned grp = t / per_group;
         const unsigned first = grp * gm;
@@ -568,7 +580,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
                 // SILU: LDS rows 64w .. 64w+31 hold gate rows o0 + 32w .., rows
                 // 64w+32 .. 64w+63 the up rows I + o0 + 32w .. (B rows from n0)
                 const int w = R >> 6, q = R & 63;
-                if constexpr (C::MX) {   // staged like A: row a_row(R), key (R >> 2) & 7
+                if constexpr (C::BL) {   // staged like A: row a_row(R), key (R >> 2) & 7
                     c.b_off[j] = uint32_t(a_row(R)) * uint32_t(p.K) + uint32_t((pc ^ ((R >> 2) & 7)) * 16);
                 } else {
                     const int brow = !SILU ? R : (q < 32 ? 32 * w + q : n_out + 32 * w + (q - 32));
@@ -595,7 +607,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         // fragment rows: A row wm*64 + 4*l16 + y lives in LDS row p0 + (y ^ odd)
         // with p0 = wm*64 + 4*l16 and odd = l16 & 1 (swizzle key l16 & 7 for
         // every y); B row wn*WN + x*16 + l16 (key l16 & 7).
-        // (MX: B rows wn*WN + 4*l16 + x in LDS rows pb + (x ^ odd), as for A)
+        // (BL: B rows wn*WN + 4*l16 + x in LDS rows pb + (x ^ odd), as for A)
         {
             const int clo = lq, chi = lq + 4;
             const int p0 = wm * 64 + 4 * l16, odd = l16 & 1;
@@ -657,7 +669,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         GFG_WAITCNT(0, 0);
         __builtin_amdgcn_s_barrier();
 
-        // ---- epilogue: lane owns row (4*l16 + y), columns 16x + 4lq .. +3 ----
+        // ---- epilogue: lane owns row (4*l16 + y); columns 16lq .. +15 (BL) or
+        // 16x + 4lq .. +3 of the wave's WN ----
         // (SILU: output columns o0 + 32*wn + 16x + 4lq .. +3 for x < FN/2, from
         // gate fragment x and up fragment x + FN/2)
         typedef OutT out4 __attribute__((ext_vector_type(4)));
@@ -666,7 +679,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             const int row = int(m0) + wm * 64 + 4 * l16 + y;   // rows of a region fit in 32 bits
             const bool ok = row < mlimit && (MASKED || int(lay[y]) == g);
             if (!ok) continue;
-            if constexpr (C::MX) {
+            if constexpr (C::BL) {
                 // lane holds columns wn*WN + 16lq + 4i + x: value acc[x][y][i]
                 typedef OutT out8 __attribute__((ext_vector_type(8)));
                 OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * p.N + n0 + wn * WN + 16 * lq;
