@@ -488,6 +488,42 @@ def grouped_gemm_mx4_masked(q_a, scale_a, q_b, scale_b, masked_m, d_init=None):
     return d
 
 
+# ---------------------------------------------------------------- a4w4 gemm1 with silu_mul
+# The third reference page's gemm1 runs on "mxfp4 (a4w4)" operands and ends in
+# the silu_mul epilogue (section "Changes", item gemm1).  Written out, it is the
+# MXFP4 grouped GEMM above followed by the silu_mul of the gemm1 section, under
+# the same gate|up reading: B[g] has 2I rows, gate rows [0, I) and up rows
+# [I, 2I), and out[m, j] = silu(h[j]) * h[I + j] with h = A_dq[m] . B_dq[g]^T.
+def grouped_gemm_mx4_silu_mul_contiguous(q_a, scale_a, q_b, scale_b, grouped_layout, out_init=None):
+    """Contiguous a4w4 gemm1 with silu_mul, float64.
+
+    q_a [M, K/2] and q_b [G, 2I, K/2] hold E2M1 codes two per byte, with
+    scales [K/32, M] and [G, K/32, 2I].  Rows with ``grouped_layout == g`` get
+    ``silu(h[:I]) * h[I:]``; padding rows keep ``out_init`` (NaN when none).
+    """
+    d = grouped_gemm_mx4_contiguous(q_a, scale_a, q_b, scale_b, grouped_layout)
+    M, half = d.shape[0], d.shape[1] // 2
+    out = np.full((M, half), np.nan) if out_init is None else np.array(out_init, dtype=np.float64)
+    layout = np.asarray(grouped_layout, dtype=np.int64)
+    rows = np.nonzero((layout >= 0) & (layout < q_b.shape[0]))[0]
+    out[rows] = _silu_mul_rows(d[rows])
+    return out
+
+
+def grouped_gemm_mx4_silu_mul_masked(q_a, scale_a, q_b, scale_b, masked_m, out_init=None):
+    """Masked a4w4 gemm1 with silu_mul, float64: q_a [G, M_max, K/2] with
+    scale_a [G, K/32, M_max]; rows ``m < masked_m[g]`` of group g get
+    ``silu(h[:I]) * h[I:]``, other rows keep ``out_init``."""
+    d = grouped_gemm_mx4_masked(q_a, scale_a, q_b, scale_b, masked_m)
+    G, Mmax, half = d.shape[0], d.shape[1], d.shape[2] // 2
+    out = np.full((G, Mmax, half), np.nan) if out_init is None else np.array(out_init, dtype=np.float64)
+    for g in range(G):
+        mm = int(min(max(int(masked_m[g]), 0), Mmax))
+        if mm:
+            out[g, :mm] = _silu_mul_rows(d[g, :mm])
+    return out
+
+
 # ---------------------------------------------------------------- metrics
 def calc_diff(x, y) -> float:
     """1 - 2*sum(x*y) / sum(x*x + y*y), in float64 ("cosine-similarity-style")."""

@@ -849,3 +849,95 @@ def test_mx4_pins_catch_planted_mistakes(monkeypatch):
         failures += 1
     monkeypatch.setattr(o.np, "clip", real_clip)
     assert failures == 3
+
+
+# ------------------------------------------------------------------ a4w4 gemm1 with silu_mul pins
+def test_mx4_silu_mul_contiguous_bruteforce_tiny():
+    """Every valid row against an fsum loop over E2M1 nibbles and the tanh
+    form of silu: gate rows [0, I), up rows [I, 2I); padding rows keep the
+    initial buffer."""
+    rng = np.random.default_rng(61)
+    layout = np.array([0, -1, 1, 1, 0, -1], np.int32)
+    K, I = 64, 12
+    a = rng.standard_normal((layout.size, K)).astype(np.float32)
+    b = rng.standard_normal((2, 2 * I, K)).astype(np.float32)
+    qa, sa = o.quantize_mx4_1x32(a)
+    qb, sb = o.quantize_mx4_1x32(b)
+    out = o.grouped_gemm_mx4_silu_mul_contiguous(qa, sa, qb, sb, layout, np.full((layout.size, I), 3.5))
+    assert out.shape == (layout.size, I)
+    for g in range(2):
+        rows = [r for r in range(layout.size) if layout[r] == g]
+        h = _bf_mx4_gemm_rows(qa, sa, qb, sb, rows, g)
+        for i, r in enumerate(rows):
+            for n in range(I):
+                ref = _tanh_silu(h[i, n]) * h[i, I + n]
+                assert abs(out[r, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+    assert np.all(out[layout < 0] == 3.5)
+
+
+def test_mx4_silu_mul_masked_bruteforce_tiny():
+    rng = np.random.default_rng(62)
+    G, Mmax, K, I = 3, 4, 64, 8
+    a = rng.standard_normal((G, Mmax, K)).astype(np.float32)
+    b = rng.standard_normal((G, 2 * I, K)).astype(np.float32)
+    masked_m = np.array([3, 0, 4], np.int32)
+    qa, sa = o.quantize_mx4_1x32(a)
+    qb, sb = o.quantize_mx4_1x32(b)
+    out = o.grouped_gemm_mx4_silu_mul_masked(qa, sa, qb, sb, masked_m, np.full((G, Mmax, I), -2.0))
+    assert out.shape == (G, Mmax, I)
+    for g in range(G):
+        mm = int(masked_m[g])
+        if mm:
+            h = _bf_mx4_gemm_rows(qa[g], sa[g], qb, sb, list(range(mm)), g)
+            for m in range(mm):
+                for n in range(I):
+                    ref = _tanh_silu(h[m, n]) * h[m, I + n]
+                    assert abs(out[g, m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
+        assert np.all(out[g, mm:] == -2.0)
+
+
+def test_mx4_silu_mul_pins_catch_planted_mistakes(monkeypatch):
+    """Planted a4w4 gemm1 mistakes (on the CPU): gate and up halves
+    exchanged, the FP8 element decode in place of E2M1's, and padding rows
+    given outputs."""
+    failures = 0
+    real_rows = o._silu_mul_rows
+
+    def swapped(d):
+        half = d.shape[-1] // 2
+        return o.silu(d[..., half:]) * d[..., :half]
+    monkeypatch.setattr(o, "_silu_mul_rows", swapped)
+    try:
+        test_mx4_silu_mul_contiguous_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "_silu_mul_rows", real_rows)
+    real_gm = o.grouped_gemm_mx4_masked
+
+    def fp8_decode(qa, sa, qb, sb, masked_m, d_init=None):
+        G, Mmax, _ = qa.shape
+        codes = np.stack([qb & 15, qb >> 4], axis=-1).reshape(*qb.shape[:-1], 2 * qb.shape[-1])
+        b = o.decode_e4m3(codes.astype(np.uint8)) * np.repeat(np.swapaxes(o.e8m0_value(sb), -1, -2), 32, axis=-1)
+        d = np.full((G, Mmax, b.shape[1]), np.nan)
+        for g in range(G):
+            mm = int(masked_m[g])
+            if mm:
+                d[g, :mm] = o.dequantize_mx4(qa[g, :mm], sa[g][:, :mm]) @ b[g].T
+        return d
+    monkeypatch.setattr(o, "grouped_gemm_mx4_masked", fp8_decode)
+    try:
+        test_mx4_silu_mul_masked_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "grouped_gemm_mx4_masked", real_gm)
+    real_sc = o.grouped_gemm_mx4_silu_mul_contiguous
+
+    def all_rows(qa, sa, qb, sb, layout, out_init=None):
+        return real_sc(qa, sa, qb, sb, np.where(np.asarray(layout) < 0, 0, layout), out_init)
+    monkeypatch.setattr(o, "grouped_gemm_mx4_silu_mul_contiguous", all_rows)
+    try:
+        test_mx4_silu_mul_contiguous_bruteforce_tiny()
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(o, "grouped_gemm_mx4_silu_mul_contiguous", real_sc)
+    assert failures == 3
