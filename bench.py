@@ -53,11 +53,11 @@ def algorithmic_bytes(w, layout=None) -> int:
     experts that have rows, both scale tensors' used parts, and D's valid rows."""
     KB, NB = w.K // 128, w.N // 128
     out_b = 2
-    out_cols = w.I if w.op == "silu_mul" else w.N
-    mx = w.op in ("mx", "mx4")
+    out_cols = w.I if w.op in ("silu_mul", "mx4_silu") else w.N
+    mx = w.op in ("mx", "mx4", "mx4_silu")
     a_scale_per_row = w.K // 32 if mx else KB
     b_scale = w.N * (w.K // 32) if mx else NB * KB
-    elem = 0.5 if w.op == "mx4" else 1.0          # bytes per A/B element
+    elem = 0.5 if w.op in ("mx4", "mx4_silu") else 1.0          # bytes per A/B element
     if w.layout == "masked":
         tiles_rows = sum(-(-min(max(m, 0), w.M_max) // 128) * 128 for m in w.masked_m)
         a_rows = sum(min(max(m, 0), w.M_max) for m in w.masked_m)
@@ -137,9 +137,10 @@ def cpu_baseline(w, x):
     from threadpoolctl import threadpool_info
     from oracle import fp8_oracle as o
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    quant_mx = o.quantize_mx4_1x32 if w.op == "mx4" else o.quantize_mx_1x32
-    gemm_mx = o.grouped_gemm_mx4_contiguous if w.op == "mx4" else o.grouped_gemm_mx_contiguous
-    if w.op in ("mx", "mx4") and w.b_distinct:
+    quant_mx = o.quantize_mx4_1x32 if w.op in ("mx4", "mx4_silu") else o.quantize_mx_1x32
+    gemm_mx = {"mx4": o.grouped_gemm_mx4_contiguous, "mx4_silu": o.grouped_gemm_mx4_silu_mul_contiguous}.get(
+        w.op, o.grouped_gemm_mx_contiguous)
+    if w.op in ("mx", "mx4", "mx4_silu") and w.b_distinct:
         n_exp = min(16, w.G)
         layout = x["grouped_layout"]
         rows = np.nonzero((layout >= 0) & (layout < n_exp))[0]
@@ -152,7 +153,8 @@ def cpu_baseline(w, x):
         flops = 2 * rows.size * w.N * w.K
         return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                 "sample": f"the rows of experts 0..{n_exp - 1} of {w.name} ({rows.size} of {w.m_valid} valid rows; "
-                          f"fp64 MX dequantize + matmul), {dt:.2f} s; quantization untimed"}
+                          f"fp64 MX dequantize + matmul{' + silu_mul' if w.op == 'mx4_silu' else ''}), {dt:.2f} s; "
+                          f"quantization untimed"}
     if w.op in ("mx", "mx4"):
         qa, sa = quant_mx(x["a"])
         qb, sb = quant_mx(x["b"])
@@ -327,7 +329,8 @@ def main():
         x = wl.draw(w, seed_offset=s)
         if s == 0:
             x0 = x
-        mxq = {"mx": gfg.fp8_quantize_mx_1x32, "mx4": gfg.fp4_quantize_mx_1x32}.get(w.op)
+        mxq = {"mx": gfg.fp8_quantize_mx_1x32, "mx4": gfg.fp4_quantize_mx_1x32,
+               "mx4_silu": gfg.fp4_quantize_mx_1x32}.get(w.op)
         if w.layout == "masked":
             qa, sa = mxq(x["a"]) if mxq else gfg.fp8_quantize_act_masked(x["a"])
             meta = torch.from_numpy(np.asarray(w.masked_m, np.int32)).to(dev)
@@ -341,7 +344,7 @@ def main():
         if w.b_distinct:      # every expert its own copy in device memory
             idx = torch.from_numpy(x["b_index"]).to(dev)
             b_dev, sb_dev = b_dev.index_select(0, idx), sb_dev.index_select(0, idx)
-        out_cols = w.I if w.op == "silu_mul" else w.N
+        out_cols = w.I if w.op in ("silu_mul", "mx4_silu") else w.N
         t = dict(a=torch.from_numpy(qa).to(dev), sa=torch.from_numpy(sa).to(dev),
                  b=b_dev, sb=sb_dev, meta=meta,
                  d=torch.empty((M_rows, out_cols), dtype=torch.bfloat16 if w.out_dtype == "bf16" else torch.float16,
@@ -356,11 +359,12 @@ def main():
     # prepared launches: pointers and sizes resolved once
     calls = []
     for t in sets:
-        silu = w.op == "silu_mul"
+        silu = w.op in ("silu_mul", "mx4_silu")
         n_arg = w.I if silu else w.N      # the silu_mul entry points take I (B has 2*I rows)
         fns = {"gemm": (gfg.raw_contiguous, gfg.raw_masked), "silu_mul": (gfg.raw_silu_mul_contiguous,
                gfg.raw_silu_mul_masked), "mx": (gfg.raw_mx_contiguous, gfg.raw_mx_masked),
-               "mx4": (gfg.raw_mx4_contiguous, gfg.raw_mx4_masked)}[w.op]
+               "mx4": (gfg.raw_mx4_contiguous, gfg.raw_mx4_masked),
+               "mx4_silu": (gfg.raw_mx4_silu_mul_contiguous, gfg.raw_mx4_silu_mul_masked)}[w.op]
         if w.layout == "masked":
             a = (t["a"].data_ptr(), t["sa"].data_ptr(), t["b"].data_ptr(), t["sb"].data_ptr(),
                  t["meta"].data_ptr(), t["d"].data_ptr(), w.G, w.M_max, n_arg, w.K, out_code, handle)
@@ -392,7 +396,7 @@ def main():
     traffic = traffic_from_profile(w)
     abytes = algorithmic_bytes(w)
     gbps = abytes / (ms * 1e-3) / 1e9
-    peak = PEAK_FP4_TFLOPS if w.op == "mx4" else PEAK_FP8_TFLOPS
+    peak = PEAK_FP4_TFLOPS if w.op in ("mx4", "mx4_silu") else PEAK_FP8_TFLOPS
     if w.flops / abytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
@@ -411,7 +415,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4e2m1" if w.op == "mx4" else "fp8e4m3",
+        "dtype": "fp4e2m1" if w.op in ("mx4", "mx4_silu") else "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": w.name, "op": w.op, "layout": w.layout, "G": w.G, "N": w.N, "K": w.K,
                    "M_rows": w.M, "M_valid": w.m_valid, "out": w.out_dtype,

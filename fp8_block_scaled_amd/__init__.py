@@ -77,6 +77,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.grouped_mxfp4_gemm_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
     lib.grouped_mxfp4_gemm_masked.restype = ctypes.c_int
     lib.fp4_quantize_mx_1x32.argtypes = [vp, i32, i64, i64, vp, vp]
+    lib.grouped_mxfp4_gemm_silu_mul_contiguous.argtypes = [vp, u8p, vp, u8p, vp, vp, i64, i64, i64, i32, i32, vp]
+    lib.grouped_mxfp4_gemm_silu_mul_contiguous.restype = ctypes.c_int
+    lib.grouped_mxfp4_gemm_silu_mul_masked.argtypes = [vp, u8p, vp, u8p, vp, vp, i32, i64, i64, i64, i32, vp]
+    lib.grouped_mxfp4_gemm_silu_mul_masked.restype = ctypes.c_int
     lib.fp4_quantize_mx_1x32.restype = ctypes.c_int
     lib.fp8_quantize_mx_1x32.restype = ctypes.c_int
     lib.fp8_quantize_act_1x128.argtypes = [vp, i64, i64, vp, vp]
@@ -140,6 +144,17 @@ def raw_mx4_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, ou
 def raw_mx4_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, stream=0) -> int:
     return load_library().grouped_mxfp4_gemm_masked(a, a_scale, b, b_scale, masked_m, d,
                                                     G, M_max, N, K, out_dtype, stream)
+
+
+def raw_mx4_silu_mul_contiguous(a, a_scale, b, b_scale, grouped_layout, d, M, I, K, G, out_dtype, stream=0) -> int:
+    """a4w4 gemm1 + silu_mul; K counts E2M1 elements, B has 2*I rows."""
+    return load_library().grouped_mxfp4_gemm_silu_mul_contiguous(a, a_scale, b, b_scale, grouped_layout, d,
+                                                                 M, I, K, G, out_dtype, stream)
+
+
+def raw_mx4_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d, G, M_max, I, K, out_dtype, stream=0) -> int:
+    return load_library().grouped_mxfp4_gemm_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d,
+                                                             G, M_max, I, K, out_dtype, stream)
 
 
 def raw_quantize_act_device(x, in_dtype, G, M, K, q, scale_t, stream=0) -> int:
@@ -449,5 +464,48 @@ def grouped_mxfp4_gemm_masked(a, a_scale, b, b_scale, masked_m, d, stream=None):
         _dev_ptr(a, "a", u8, dev), _dev_ptr(a_scale, "a_scale", u8, dev), _dev_ptr(b, "b", u8, dev),
         _dev_ptr(b_scale, "b_scale", u8, dev), _dev_ptr(masked_m, "masked_m", (torch.int32,), dev),
         _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev), G, Mmax, N, K, _out_code(d),
+        _stream_handle(stream, dev)))
+    return d
+
+
+def grouped_mxfp4_gemm_silu_mul_contiguous(a, a_scale, b, b_scale, grouped_layout, d, stream=None):
+    """a4w4 gemm1 + silu_mul, contiguous layout: a [M, K/2] uint8 (E2M1 pairs), a_scale [K/32, M],
+    b [G, 2I, K/2] (gate rows then up rows), b_scale [G, K/32, 2I], d [M, I]: for rows of
+    expert g, ``h = A[row] . B[g]^T`` and ``d[row] = silu(h[:I]) * h[I:]``."""
+    torch = _torch()
+    dev = d.device
+    M, Kh = a.shape
+    G, N2, Kb = b.shape
+    K = 2 * Kh
+    if N2 % 2 or Kb != Kh or tuple(d.shape) != (M, N2 // 2) or tuple(grouped_layout.shape) != (M,):
+        raise ValueError("shape mismatch between a, b [G, 2I, K/2], grouped_layout and d [M, I]")
+    if tuple(a_scale.shape) != (K // 32, M) or tuple(b_scale.shape) != (G, K // 32, N2):
+        raise ValueError("scale tensor shapes do not match the MX (1,32) layouts")
+    u8 = (torch.uint8,)
+    _check(raw_mx4_silu_mul_contiguous(
+        _dev_ptr(a, "a", u8, dev), _dev_ptr(a_scale, "a_scale", u8, dev), _dev_ptr(b, "b", u8, dev),
+        _dev_ptr(b_scale, "b_scale", u8, dev), _dev_ptr(grouped_layout, "grouped_layout", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev), M, N2 // 2, K, G, _out_code(d),
+        _stream_handle(stream, dev)))
+    return d
+
+
+def grouped_mxfp4_gemm_silu_mul_masked(a, a_scale, b, b_scale, masked_m, d, stream=None):
+    """a4w4 gemm1 + silu_mul, masked layout: a [G, M_max, K/2], a_scale [G, K/32, M_max],
+    b [G, 2I, K/2], b_scale [G, K/32, 2I], masked_m [G] int32 (device), d [G, M_max, I]."""
+    torch = _torch()
+    dev = d.device
+    G, Mmax, Kh = a.shape
+    Gb, N2, Kb = b.shape
+    K = 2 * Kh
+    if N2 % 2 or Gb != G or Kb != Kh or tuple(d.shape) != (G, Mmax, N2 // 2) or tuple(masked_m.shape) != (G,):
+        raise ValueError("shape mismatch between a, b [G, 2I, K/2], masked_m and d [G, M_max, I]")
+    if tuple(a_scale.shape) != (G, K // 32, Mmax) or tuple(b_scale.shape) != (G, K // 32, N2):
+        raise ValueError("scale tensor shapes do not match the MX (1,32) layouts")
+    u8 = (torch.uint8,)
+    _check(raw_mx4_silu_mul_masked(
+        _dev_ptr(a, "a", u8, dev), _dev_ptr(a_scale, "a_scale", u8, dev), _dev_ptr(b, "b", u8, dev),
+        _dev_ptr(b_scale, "b_scale", u8, dev), _dev_ptr(masked_m, "masked_m", (torch.int32,), dev),
+        _dev_ptr(d, "d", (torch.bfloat16, torch.float16), dev), G, Mmax, N2 // 2, K, _out_code(d),
         _stream_handle(stream, dev)))
     return d

@@ -166,7 +166,10 @@ struct TileCtx {
     // tile interleaves gate and up rows.
     static constexpr bool BL = MX || (!SILU_ && BN_ == 256);
     // gemm1 with silu_mul: the B tile holds gate and up rows, and fragments
-    // x < FN/2 (gate) take the gate block's scale, x >= FN/2 (up) the up block's
+    // x < FN/2 (gate) take the gate block's scale, x >= FN/2 (up) the up block's.
+    // (MXFP4: B is staged like A and every row carries its own scales, so
+    // lanes with lq < 2 end up with gate values and lanes lq + 2 with the up
+    // values of the same columns.)
     static constexpr bool SILU = SILU_;
     static constexpr int WAVES = NTHREADS / 64;
     static constexpr int WN = BN / 4;               // columns per wave (2 x 4 wave grid)
@@ -237,7 +240,7 @@ __device__ __forceinline__ void issue_stage(const C& c, GFG_LDS uint8_t* __restr
         sb = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off, uint32_t(kb) * c.sb_stride, 0));
     else
         sb = load_scale_word(c.sb_row, kb);
-    if constexpr (C::SILU) sbu = load_scale_word(c.sbu_row, kb);
+    if constexpr (C::SILU && !C::MX) sbu = load_scale_word(c.sbu_row, kb);
     if constexpr (C::MX4) {
         sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(c.sa_rsrc, c.sa_off[1], uint32_t(kb) * c.sa_stride, 0));
         sbu = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off1, uint32_t(kb) * c.sb_stride, 0));
@@ -395,7 +398,7 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
             sb = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off, uint32_t(kb_refill) * c.sb_stride, 0));
         else
             sb = load_scale_word(c.sb_row, kb_refill);
-        if constexpr (C::SILU) sbu = load_scale_word(c.sbu_row, kb_refill);
+        if constexpr (C::SILU && !C::MX) sbu = load_scale_word(c.sbu_row, kb_refill);
         if constexpr (C::MX4) {
             sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(c.sa_rsrc, c.sa_off[1], uint32_t(kb_refill) * c.sa_stride,
                                                              0));
@@ -433,7 +436,8 @@ __device__ __forceinline__ v4f silu_mul4(v4f gv, v4f uv) {
 template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU, bool MX, bool MX4 = false>
 __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p) {
     static_assert(!SILU || BN == 256, "the gate/up interleave assumes 64 B rows per wave");
-    static_assert(!(MX || MX4) || (BN == 256 && SAW && !SILU), "MX runs on the 256-column tile with packed scale words");
+    static_assert(!(MX || MX4) || (BN == 256 && SAW && (!SILU || MX4)),
+                  "MX runs on the 256-column tile with packed scale words; silu_mul with MXFP4 only");
     using C = TileCtx<BN, SAW, SILU, MX, MX4>;
     constexpr int FN = C::FN, FM = C::FM, WN = C::WN;
     constexpr int L = C::LOADS;
@@ -551,7 +555,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             // 4*l16 .. +3 of block 4*kb + lq (MX4: 8*kb + lq, and 8*kb + 4 + lq)
             const int64_t sbe = int64_t(g) * SKB * p.N;
             c.sb_rsrc = make_rsrc(p.b_scale + sbe + n0, uint32_t(int64_t(SKB) * p.N - n0));
-            c.sb_off = uint32_t(lq * p.N + wn * WN + 4 * l16);
+            // (SILU: the lane's four rows are gate rows 32*wn + 4*l16 .. for
+            // l16 < 8 and up rows n_out + 32*wn + 4*(l16 - 8) .. otherwise)
+            const int brow4 = !SILU ? wn * WN + 4 * l16 : (l16 < 8 ? 32 * wn + 4 * l16 : n_out + 32 * wn + 4 * (l16 - 8));
+            c.sb_off = uint32_t(lq * p.N + brow4);
             c.sb_off1 = c.sb_off + uint32_t(4 * p.N);
             c.sb_stride = uint32_t((MX4 ? 8 : 4) * p.N);
         } else if constexpr (SILU) {
@@ -581,7 +588,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
                 // 64w+32 .. 64w+63 the up rows I + o0 + 32w .. (B rows from n0)
                 const int w = R >> 6, q = R & 63;
                 if constexpr (C::BL) {   // staged like A: row a_row(R), key (R >> 2) & 7
-                    c.b_off[j] = uint32_t(a_row(R)) * uint32_t(p.K) + uint32_t((pc ^ ((R >> 2) & 7)) * 16);
+                    const int ar = a_row(R), aw = ar >> 6, aq = ar & 63;   // a_row stays in R's 4-row group
+                    const int brow = !SILU ? ar : (aq < 32 ? 32 * aw + aq : n_out + 32 * aw + (aq - 32));
+                    c.b_off[j] = uint32_t(brow) * uint32_t(p.K) + uint32_t((pc ^ ((R >> 2) & 7)) * 16);
                 } else {
                     const int brow = !SILU ? R : (q < 32 ? 32 * w + q : n_out + 32 * w + (q - 32));
                     c.b_off[j] = uint32_t(brow) * uint32_t(p.K) + uint32_t((pc ^ rr) * 16);
@@ -674,6 +683,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         // (SILU: output columns o0 + 32*wn + 16x + 4lq .. +3 for x < FN/2, from
         // gate fragment x and up fragment x + FN/2)
         typedef OutT out4 __attribute__((ext_vector_type(4)));
+        if constexpr (SILU && C::MX) {
+            // lanes lq < 2 hold the gate values of wave columns 16lq + 4i + x,
+            // lanes lq + 2 (32 lanes up) the up values of the same columns:
+            // each lane reads its partner's accumulators through ds_bpermute
+            const int partner = (lane ^ 32) * 4;
+            v4f up[FN][FM];
+#pragma unroll
+            for (int x = 0; x < FN; ++x)
+#pragma unroll
+                for (int y = 0; y < FM; ++y)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // (the element goes through a scalar first: a bit_cast of
+                        // a vector-element expression reads element 0 here)
+                        const float e = acc[x][y][i];
+                        up[x][y][i] = __builtin_bit_cast(
+                            float, __builtin_amdgcn_ds_bpermute(partner, __builtin_bit_cast(int, e)));
+                    }
+            if (lq < 2) {
+                typedef OutT out8 __attribute__((ext_vector_type(8)));
+                typedef float f8v __attribute__((ext_vector_type(8)));
+#pragma unroll
+                for (int y = 0; y < FM; ++y) {
+                    const int row = int(m0) + wm * 64 + 4 * l16 + y;
+                    const bool ok = row < mlimit && (MASKED || int(lay[y]) == g);
+                    if (!ok) continue;
+                    const v4f c0 = silu_mul4(acc[0][y], up[0][y]), c1 = silu_mul4(acc[1][y], up[1][y]);
+                    const v4f c2 = silu_mul4(acc[2][y], up[2][y]), c3 = silu_mul4(acc[3][y], up[3][y]);
+                    OutT* drow = reinterpret_cast<OutT*>(d_reg) + int64_t(row) * n_out + n0 + wn * (WN / 2) + 16 * lq;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f8v v = {c0[2 * h], c1[2 * h], c2[2 * h], c3[2 * h],
+                                       c0[2 * h + 1], c1[2 * h + 1], c2[2 * h + 1], c3[2 * h + 1]};
+                        *reinterpret_cast<out8*>(drow + 8 * h) = __builtin_convertvector(v, out8);
+                    }
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int y = 0; y < FM; ++y) {
             const int row = int(m0) + wm * 64 + 4 * l16 + y;   // rows of a region fit in 32 bits
@@ -868,6 +916,12 @@ int dispatch_mx(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) 
 }
 
 template <bool MASKED>
+int dispatch_mx4_silu(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
+    return out_dtype == GFG_OUT_BF16 ? launch_t<256, MASKED, true, __bf16, true, false, true>(p, n_cand, s)
+                                     : launch_t<256, MASKED, true, _Float16, true, false, true>(p, n_cand, s);
+}
+
+template <bool MASKED>
 int dispatch_silu(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
     return out_dtype == GFG_OUT_BF16 ? launch_t<256, MASKED, true, __bf16, true>(p, n_cand, s)
                                      : launch_t<256, MASKED, true, _Float16, true>(p, n_cand, s);
@@ -1002,4 +1056,43 @@ extern "C" int grouped_mxfp4_gemm_masked(const void* a, const uint8_t* a_scale, 
     if (int rc = check_mx(fn, N, M_max, a_scale, b_scale)) return rc;
     if (M_max == 0) return GFG_OK;
     return dispatch_mx<true, true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
+}
+
+// a4w4 gemm1 with silu_mul: B [G][2I][K/2] E2M1 (gate rows, then up rows),
+// output [rows][I].  K counts E2M1 elements (a multiple of 256), I a multiple
+// of 128.
+extern "C" int grouped_mxfp4_gemm_silu_mul_contiguous(const void* a, const uint8_t* a_scale, const void* b,
+                                                      const uint8_t* b_scale, const int32_t* grouped_layout,
+                                                      void* d, int64_t M, int64_t I, int64_t K, int32_t G,
+                                                      int32_t out_dtype, void* stream) {
+    clear_error();
+    const char* fn = "grouped_mxfp4_gemm_silu_mul_contiguous";
+    if (int rc = check_k4(fn, K)) return rc;
+    if (int rc = check_silu(fn, I, M < 0 ? 0 : M, a_scale)) return rc;
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, 2 * I, K / 2, G, out_dtype, &p,
+                               &n_cand))
+        return rc;
+    if (int rc = check_mx(fn, 2 * I, M, a_scale, b_scale)) return rc;
+    if (M == 0) return GFG_OK;
+    return dispatch_mx4_silu<false>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int grouped_mxfp4_gemm_silu_mul_masked(const void* a, const uint8_t* a_scale, const void* b,
+                                                  const uint8_t* b_scale, const int32_t* masked_m, void* d,
+                                                  int32_t G, int64_t M_max, int64_t I, int64_t K,
+                                                  int32_t out_dtype, void* stream) {
+    clear_error();
+    const char* fn = "grouped_mxfp4_gemm_silu_mul_masked";
+    if (int rc = check_k4(fn, K)) return rc;
+    if (int rc = check_silu(fn, I, M_max < 0 ? 0 : M_max, a_scale)) return rc;
+    Params p;
+    int64_t n_cand = 0;
+    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, 2 * I, K / 2, out_dtype, &p,
+                               &n_cand))
+        return rc;
+    if (int rc = check_mx(fn, 2 * I, M_max, a_scale, b_scale)) return rc;
+    if (M_max == 0) return GFG_OK;
+    return dispatch_mx4_silu<true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
 }

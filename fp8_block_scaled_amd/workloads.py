@@ -53,7 +53,8 @@ class Workload:
     M_max: int = 0                                    # masked: rows per group buffer
     masked_m: list = field(default_factory=list)      # masked: valid rows per group
     row_log10_range: tuple | None = None              # per-token magnitude 10**U(lo, hi)
-    op: str = "gemm"                                  # "gemm", "silu_mul" (N = 2*I), "mx" / "mx4" (MXFP8 / MXFP4)
+    op: str = "gemm"                                  # "gemm", "silu_mul" (N = 2*I), "mx" / "mx4" (MXFP8 / MXFP4),
+                                                      # "mx4_silu" (MXFP4 gemm1 with silu_mul, N = 2*I)
     b_distinct: int = 0                               # > 0: expert g's B is draw g % b_distinct
 
     @property
@@ -135,7 +136,8 @@ def gemm1_workloads() -> list[Workload]:
 def mx_workloads() -> list[Workload]:
     """MX GEMMs: the benchmarked contiguous shape and the Kimi-K2.5 TP=4 gemm1
     shape without its epilogue, in MXFP8 (seeds 1007, 1008) and in MXFP4, the
-    page's a4w4 (seeds 1009, 1010); N(0,1) data."""
+    page's a4w4 (seeds 1009, 1010); and the Kimi gemm1 as the page runs it,
+    a4w4 with silu_mul (seed 1011, B [2I, K] with I = 512); N(0,1) data."""
     return [Workload("mx_contig_g4_m1024_n2048_k7168", "contiguous", 4, 2048, 7168, "bf16", 1007,
                      m_per_group=[1024] * 4, op="mx"),
             Workload("mx_kimi_tp4_gemm1_t4096", "contiguous", 385, 1024, 7168, "bf16", 1008,
@@ -143,7 +145,9 @@ def mx_workloads() -> list[Workload]:
             Workload("mx4_contig_g4_m1024_n2048_k7168", "contiguous", 4, 2048, 7168, "bf16", 1009,
                      m_per_group=[1024] * 4, op="mx4"),
             Workload("mx4_kimi_tp4_gemm1_t4096", "contiguous", 385, 1024, 7168, "bf16", 1010,
-                     m_per_group=_topk_counts(_rng(1010), 4096, 385, 9), op="mx4", b_distinct=8)]
+                     m_per_group=_topk_counts(_rng(1010), 4096, 385, 9), op="mx4", b_distinct=8),
+            Workload("mx4_silu_kimi_tp4_gemm1_t4096", "contiguous", 385, 1024, 7168, "bf16", 1011,
+                     m_per_group=_topk_counts(_rng(1011), 4096, 385, 9), op="mx4_silu", b_distinct=8)]
 
 
 def workload(name_or_index) -> Workload:

@@ -203,6 +203,39 @@ GFG_API int grouped_mxfp4_gemm_masked(const void* a, const uint8_t* a_scale,
                               int32_t out_dtype, void* stream);
 
 /*
+ * a4w4 gemm1 with silu_mul: the gemm1 of the third reference page as the
+ * page runs it ("mxfp4 (a4w4)" operands, section "Summary"; the silu_mul
+ * epilogue, section "Changes", item gemm1).  The operands are those of the
+ * MXFP4 GEMM above; the epilogue is that of grouped_fp8_gemm_silu_mul_*:
+ * each expert's B holds 2*I rows, gate rows [0, I) then up rows [I, 2*I),
+ * and for every computed row m
+ *
+ *   h = A[m] . B[g]^T  (length 2*I, fp32),   out[m, j] = silu(h[j]) * h[I + j]
+ *
+ *   a         contiguous [M][K/2], masked [G][M_max][K/2]      E2M1, two per byte
+ *   b         [G][2*I][K/2]                                    (gate rows, then up rows)
+ *   a_scale   contiguous [K/32][M], masked [G][K/32][M_max]    E8M0 bytes
+ *   b_scale   [G][K/32][2*I]
+ *   d         contiguous [M][I], masked [G][M_max][I]          bf16 or f16
+ *   (grouped_layout, masked_m, out_dtype, stream as in the GEMMs)
+ *
+ * Sizes: K (E2M1 elements) a multiple of 256, I a positive multiple of 128,
+ * M (M_max) a multiple of 4, both scale tensors 4-byte aligned (else
+ * GFG_EUNSUPPORTED; I <= 0 or K <= 0 is GFG_EINVAL).  Rows are chosen as in
+ * the GEMMs; other rows of d are left untouched.
+ */
+GFG_API int grouped_mxfp4_gemm_silu_mul_contiguous(const void* a, const uint8_t* a_scale,
+                                           const void* b, const uint8_t* b_scale,
+                                           const int32_t* grouped_layout, void* d,
+                                           int64_t M, int64_t I, int64_t K, int32_t G,
+                                           int32_t out_dtype, void* stream);
+GFG_API int grouped_mxfp4_gemm_silu_mul_masked(const void* a, const uint8_t* a_scale,
+                                       const void* b, const uint8_t* b_scale,
+                                       const int32_t* masked_m, void* d,
+                                       int32_t G, int64_t M_max, int64_t I, int64_t K,
+                                       int32_t out_dtype, void* stream);
+
+/*
  * MXFP4 quantizer (CPU, synchronous):
  *   x [G][R][K] float -> q [G][R][K/2] (two E2M1 codes per byte), scale_t [G][K/32][R] E8M0.
  * Per row and 32-wide K block: t = floor(log2(max|x|)) - 2 (t = 0 for an

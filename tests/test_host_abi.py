@@ -349,3 +349,31 @@ def test_mx4_gemm_argument_errors(contig):
     assert call(M=130) == 2
     assert call(sb=FAKE + 2) == 2
     assert call(M=0) == 0
+
+
+# ------------------------------------------------------------------ a4w4 gemm1 with silu_mul
+@pytest.mark.parametrize("contig", [True, False])
+def test_mx4_silu_mul_argument_errors(contig):
+    def call(**kw):
+        a = dict(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, meta=FAKE, d=FAKE, M=256, I=256, K=512, G=2, dt=0)
+        a.update(kw)
+        if contig:
+            return gfg.raw_mx4_silu_mul_contiguous(a["a"], a["sa"], a["b"], a["sb"], a["meta"], a["d"], a["M"],
+                                                   a["I"], a["K"], a["G"], a["dt"], 0)
+        return gfg.raw_mx4_silu_mul_masked(a["a"], a["sa"], a["b"], a["sb"], a["meta"], a["d"], a["G"], a["M"],
+                                           a["I"], a["K"], a["dt"], 0)
+    for k in ("a", "sa", "b", "sb", "meta", "d"):
+        assert call(**{k: None}) == 1, k
+    assert call(dt=2) == 1
+    assert call(G=0) == 1
+    assert call(K=0) == 1
+    assert call(I=0) == 1
+    assert call(K=384) == 2            # K (E2M1 elements) must be a multiple of 256
+    assert "multiple of 256" in gfg.load_library().gfg_last_error().decode()
+    assert call(I=192) == 2            # I must be a multiple of 128 (the output tile)
+    assert "multiple of 128" in gfg.load_library().gfg_last_error().decode()
+    assert call(M=130) == 2            # scale rows not a multiple of 4
+    assert call(sa=FAKE + 2) == 2
+    assert call(sb=FAKE + 2) == 2
+    assert call(M=0) == 0
+    assert call(M=-4) == 1
