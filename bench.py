@@ -131,71 +131,69 @@ def summarize_traffic(workload, fetch_dir, write_dir, copy_bytes):
     print(json.dumps(out, indent=1))
 
 
+CPU_MIN_SECONDS = 10.0   # the oracle repeats its sample until this much host time has passed
+
+
+def _repeat_timed(fn):
+    """Run fn until CPU_MIN_SECONDS have passed (at least once): (seconds per run, runs)."""
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_MIN_SECONDS:
+            return dt / runs, runs
+
+
 def cpu_baseline(w, x):
     """The fp64 oracle (dequantize, then matmul) on the same workload, timed on
-    the host.  Its own quantizer prepares the operands outside the timing."""
+    the host.  Its own quantizer prepares the operands outside the timing; the
+    timed sample repeats until at least CPU_MIN_SECONDS of host time."""
     from threadpoolctl import threadpool_info
     from oracle import fp8_oracle as o
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     quant_mx = o.quantize_mx4_1x32 if w.op in ("mx4", "mx4_silu") else o.quantize_mx_1x32
     gemm_mx = {"mx4": o.grouped_gemm_mx4_contiguous, "mx4_silu": o.grouped_gemm_mx4_silu_mul_contiguous}.get(
         w.op, o.grouped_gemm_mx_contiguous)
-    if w.op in ("mx", "mx4", "mx4_silu") and w.b_distinct:
+
+    def result(flops, dt, runs, what):
+        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{what}, {dt:.2f} s per run, {runs} runs; quantization untimed"}
+
+    if w.op in ("silu_mul", "mx4_silu") or (w.op in ("mx", "mx4") and w.b_distinct):
+        # bounded sample: the rows of the first 16 experts (all 385 weight
+        # matrices would be 22 GB in float64)
         n_exp = min(16, w.G)
         layout = x["grouped_layout"]
         rows = np.nonzero((layout >= 0) & (layout < n_exp))[0]
-        qa, sa = quant_mx(x["a"][rows])
-        qb_d, sb_d = quant_mx(x["b"])
-        sel = x["b_index"][:n_exp]
-        t0 = time.perf_counter()
-        gemm_mx(qa, sa, qb_d[sel], sb_d[sel], layout[rows])
-        dt = time.perf_counter() - t0
-        flops = 2 * rows.size * w.N * w.K
-        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-                "sample": f"the rows of experts 0..{n_exp - 1} of {w.name} ({rows.size} of {w.m_valid} valid rows; "
-                          f"fp64 MX dequantize + matmul{' + silu_mul' if w.op == 'mx4_silu' else ''}), {dt:.2f} s; "
-                          f"quantization untimed"}
+        sel = x["b_index"][:n_exp] if "b_index" in x else np.arange(n_exp)
+        if w.op == "silu_mul":
+            qa, sa = o.quantize_act_1x128(x["a"][rows])
+            qb_d, sb_d = o.quantize_weight_128x128(x["b"])
+            fn = lambda: o.grouped_gemm_silu_mul_contiguous(qa, sa, qb_d[sel], sb_d[sel], layout[rows])
+            what = "fp64 dequantize + matmul + silu_mul"
+        else:
+            qa, sa = quant_mx(x["a"][rows])
+            qb_d, sb_d = quant_mx(x["b"])
+            fn = lambda: gemm_mx(qa, sa, qb_d[sel], sb_d[sel], layout[rows])
+            what = "fp64 MX dequantize + matmul" + (" + silu_mul" if w.op == "mx4_silu" else "")
+        dt, runs = _repeat_timed(fn)
+        return result(2 * rows.size * w.N * w.K, dt, runs,
+                      f"the rows of experts 0..{n_exp - 1} of {w.name} ({rows.size} of {w.m_valid} valid rows; {what})")
     if w.op in ("mx", "mx4"):
         qa, sa = quant_mx(x["a"])
         qb, sb = quant_mx(x["b"])
-        t0 = time.perf_counter()
-        gemm_mx(qa, sa, qb, sb, x["grouped_layout"])
-        dt = time.perf_counter() - t0
-        return {"value": round(w.flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-                "sample": f"one full step of {w.name} (fp64 MX dequantize + matmul over all valid rows), "
-                          f"{dt:.2f} s; quantization untimed"}
-    if w.op == "silu_mul":
-        # bounded sample: the rows of the first 16 experts (the full weight set
-        # would be 22 GB in float64)
-        n_exp = min(16, w.G)
-        layout = x["grouped_layout"]
-        rows = np.nonzero((layout >= 0) & (layout < n_exp))[0]
-        qa, sa = o.quantize_act_1x128(x["a"][rows])
-        qb_d, sb_d = o.quantize_weight_128x128(x["b"])
-        sel = x["b_index"][:n_exp]
-        t0 = time.perf_counter()
-        o.grouped_gemm_silu_mul_contiguous(qa, sa, qb_d[sel], sb_d[sel], layout[rows])
-        dt = time.perf_counter() - t0
-        flops = 2 * rows.size * w.N * w.K
-        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-                "sample": f"the rows of experts 0..{n_exp - 1} of {w.name} ({rows.size} of {w.m_valid} valid rows; "
-                          f"fp64 dequantize + matmul + silu_mul), {dt:.2f} s; quantization untimed"}
+        dt, runs = _repeat_timed(lambda: gemm_mx(qa, sa, qb, sb, x["grouped_layout"]))
+        return result(w.flops, dt, runs, f"full steps of {w.name} (fp64 MX dequantize + matmul over all valid rows)")
     if w.layout == "masked":
         qa, sa = o.quantize_act_masked(x["a"])
         qb, sb = o.quantize_weight_128x128(x["b"])
-        t0 = time.perf_counter()
-        o.grouped_gemm_masked(qa, sa, qb, sb, w.masked_m)
-        dt = time.perf_counter() - t0
+        dt, runs = _repeat_timed(lambda: o.grouped_gemm_masked(qa, sa, qb, sb, w.masked_m))
     else:
         qa, sa = o.quantize_act_1x128(x["a"])
         qb, sb = o.quantize_weight_128x128(x["b"])
-        t0 = time.perf_counter()
-        o.grouped_gemm_contiguous(qa, sa, qb, sb, x["grouped_layout"])
-        dt = time.perf_counter() - t0
-    return {"value": round(w.flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"one full step of {w.name} (fp64 dequantize + matmul over all valid rows), "
-                      f"{dt:.2f} s; quantization untimed"}
+        dt, runs = _repeat_timed(lambda: o.grouped_gemm_contiguous(qa, sa, qb, sb, x["grouped_layout"]))
+    return result(w.flops, dt, runs, f"full steps of {w.name} (fp64 dequantize + matmul over all valid rows)")
 
 
 def quant_bytes(G, M, K, in_size):
