@@ -285,8 +285,8 @@ GFG_API int fp8_quantize_weight_128x128(const float* w, int32_t G, int64_t N, in
  * t = -127 (which still keeps |x / 2^t| <= 448).
  *
  * Sizes: G in [1, 65535]; M, K >= 0 (either 0 is a no-op); K a multiple of
- * 128 and M, K <= 2^30 (else GFG_EUNSUPPORTED).  The library allocates and
- * synchronizes nothing.
+ * 128, M <= 2^30, K <= 2^24 and G * ceil(M/32) * K/128 < 2^31 - 64 (else
+ * GFG_EUNSUPPORTED).  The library allocates and synchronizes nothing.
  */
 GFG_API int fp8_quantize_act_1x128_device(const void* x, int32_t in_dtype, int32_t G, int64_t M, int64_t K,
                                           uint8_t* q, uint8_t* scale_t, void* stream);

@@ -46,7 +46,8 @@ def _oracle(x):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(1, 128), (7, 256), (65, 384), (130, 1152), (257, 2304), (3, 70, 384)])
+@pytest.mark.parametrize("shape", [(1, 128), (7, 256), (65, 384), (130, 1152), (257, 2304), (3, 70, 384),
+                                   (2, 20001, 1152)])
 def test_device_quant_bit_exact(shape, dtype):
     print(f"[quant] shape={shape} dtype={dtype}", flush=True)
     x = _draw(shape, seed=sum(shape))

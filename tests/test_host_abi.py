@@ -122,6 +122,10 @@ def test_device_quantizer_argument_errors():
     assert q(None, 1, 1, 4, 0, None, None) == 0
     assert q(None, 0, 1, 4, 128, 0x1000, 0x1000) == 1            # null x
     assert q(0x1000, 0, 1, 4, 200, 0x1000, 0x1000) == 2          # K not a multiple of 128
+    assert q(0x1000, 0, 1, 4, (1 << 24) + 128, 0x1000, 0x1000) == 2   # K above 2^24
+    assert q(0x1000, 0, 1, (1 << 30) + 1, 128, 0x1000, 0x1000) == 2   # M above 2^30
+    assert q(0x1000, 0, 65535, 1 << 20, 1 << 14, 0x1000, 0x1000) == 2  # 2^31 or more triples
+    assert "2^31" in gfg.load_library().gfg_last_error().decode()
     assert q(0x1008, 0, 1, 4, 128, 0x1000, 0x1000) == 1          # x not 16-byte aligned
     assert "16-byte" in gfg.load_library().gfg_last_error().decode()
 
