@@ -36,13 +36,14 @@ PEAK_HBM_GBS = 8000.0
 RIDGE_FLOP_PER_BYTE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 DEFAULT_WORKLOAD = "contig_g4_m1024_n2048_k7168"
 KERNEL_SRC = os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", "gfg_gemm.hip")
+QUANT_SRC = os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", "gfg_quant.hip")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path=KERNEL_SRC) -> str:
     """Hash of the kernel source's code: // comments and blank lines removed,
     so an edit to comments alone keeps stored counter results valid."""
     import re
-    with open(KERNEL_SRC) as f:
+    with open(path) as f:
         lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
     code = "\n".join(ln for ln in lines if ln)
     return hashlib.sha256(code.encode()).hexdigest()[:16]
@@ -100,17 +101,31 @@ def _pmc_per_dispatch(root, counter):
     return {k: (sum(d.values()) / len(d), len(d)) for k, d in per.items()}
 
 
-def summarize_traffic(workload, fetch_dir, write_dir, copy_bytes):
-    """HBM bytes per launch of the GEMM kernel: FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch) divided by what the same counter reads per byte for the plain copy
-    kernel of known size that the run also launched."""
+def quant_traffic_path(w, in_dtype):
+    return os.path.join(ROOT, "profiles", f"traffic_quant_{w.name}_{in_dtype}.json")
+
+
+def summarize_traffic(workload, fetch_dir, write_dir, copy_bytes, quant_in=None):
+    """HBM bytes per launch of the GEMM kernel (or, with quant_in, of the device
+    quantizer on the workload's A operand in that input dtype): FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) divided by what the same counter reads per
+    byte for the plain copy kernel of known size that the run also launched."""
     from fp8_block_scaled_amd import workloads as wl
     w = wl.workload(workload)
-    out = {"workload": w.name, "kernel_source_sha256_16": kernel_source_hash()}
+    if quant_in:
+        a = wl.draw(w)["a"]
+        G, M, K = (1, *a.shape) if a.ndim == 2 else a.shape
+        algo, path, src, match = (quant_bytes(G, M, K, 2 if quant_in == "bf16" else 4),
+                                  quant_traffic_path(w, quant_in), QUANT_SRC, "quant_act_1x128")
+    else:
+        algo, path, src, match = (algorithmic_bytes(w), os.path.join(ROOT, "profiles", f"traffic_{w.name}.json"),
+                                  KERNEL_SRC, "grouped_fp8_gemm")
+    out = {"workload": w.name if not quant_in else f"quant_act_1x128 of {w.name}.a ({quant_in})",
+           "kernel_source_sha256_16": kernel_source_hash(src)}
     total = 0.0
     for counter, root in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _pmc_per_dispatch(root, counter)
-        gemm = [v for k, v in per.items() if "grouped_fp8_gemm" in k]
+        gemm = [v for k, v in per.items() if match in k]
         copy = [(k, v) for k, v in per.items() if "neg" in k.lower()]
         if not gemm or not copy:
             raise SystemExit(f"{counter}: need both the GEMM and the copy kernel in {root}: {list(per)}")
@@ -118,13 +133,13 @@ def summarize_traffic(workload, fetch_dir, write_dir, copy_bytes):
         factor = cval * 1024.0 / copy_bytes
         gbytes = gemm[0][0] * 1024.0 / factor
         total += gbytes
-        out[counter] = {"gemm_KiB_per_dispatch": round(gemm[0][0], 1), "gemm_dispatches": gemm[0][1],
+        kk = "quant" if quant_in else "gemm"
+        out[counter] = {f"{kk}_KiB_per_dispatch": round(gemm[0][0], 1), f"{kk}_dispatches": gemm[0][1],
                         "copy_kernel": ck, "copy_bytes": copy_bytes, "copy_KiB_per_dispatch": round(cval, 1),
-                        "factor": round(factor, 4), "gemm_bytes_per_launch": int(gbytes)}
+                        "factor": round(factor, 4), f"{kk}_bytes_per_launch": int(gbytes)}
     out["hbm_bytes_per_launch"] = int(total)
-    out["algorithmic_bytes_per_launch"] = algorithmic_bytes(w)
-    out["traffic_over_algorithmic"] = round(total / algorithmic_bytes(w), 3)
-    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    out["algorithmic_bytes_per_launch"] = algo
+    out["traffic_over_algorithmic"] = round(total / algo, 3)
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
@@ -202,6 +217,19 @@ def quant_bytes(G, M, K, in_size):
     return G * M * K * (in_size + 1) + G * M * (K // 128)
 
 
+def quant_traffic(w, in_dtype):
+    """HBM bytes per call of the device quantizer from stored counter runs, if
+    they were taken on the current quantizer source (else None)."""
+    path = quant_traffic_path(w, in_dtype)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(QUANT_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 def bench_quant(args):
     """The device activation quantizer on a workload's A operand (bf16 or f32
     input), timed with HIP events on its stream; HBM-bound, priced against
@@ -257,20 +285,27 @@ def bench_quant(args):
         "config": {"workload": f"quant_act_1x128 of {w.name}.a", "G": G, "M": M, "K": K,
                    "in": args.in_dtype, "input_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": quant_traffic(w, args.in_dtype)},
         "algorithmic_bytes_per_step": per_set,
     }
     if not args.no_cpu:
         rows = min(M, 8192)
         xs0 = xs[0][0, :rows].float().cpu().numpy()
-        t0 = time.perf_counter()
-        o.quantize_act_1x128(xs0)
-        dtc = time.perf_counter() - t0
+        dtc, runs = _repeat_timed(lambda: o.quantize_act_1x128(xs0))
         res["cpu_baseline"] = {"value": round(quant_bytes(1, rows, K, in_size) / dtc / 1e9, 3), "unit": "GB/s",
                                "cores": 1, "kind": "oracle",
                                "sample": f"oracle quantize_act_1x128 on the first {rows} rows of group 0 "
-                                         f"({rows}x{K}), {dtc:.2f} s"}
+                                         f"({rows}x{K}), {dtc:.2f} s per run, {runs} runs"}
     print(json.dumps(res), flush=True)
+    if args.copy_bytes:
+        del xs, qs, ss, calls
+        # the calibration kernel of the counter passes: reads and writes copy_bytes each call
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize(dev)
 
 
 def main():
@@ -297,6 +332,11 @@ def main():
     if args.op == "quant":
         if args.gpus != 1:
             raise SystemExit("this benchmark runs on one GPU only")
+        if args.traffic_from:
+            if not args.copy_bytes:
+                raise SystemExit("--traffic-from needs the --copy-bytes the counter runs used")
+            summarize_traffic(args.workload, *args.traffic_from, args.copy_bytes, quant_in=args.in_dtype)
+            return
         bench_quant(args)
         return
     if args.traffic_from:
