@@ -24,7 +24,7 @@
 // the end of M fall outside the descriptor, where the hardware returns zeros
 // for loads and drops stores.  With no predicated branches around the memory
 // operations, the compiler's counter waits stay exact (wait for the item being
-// encoded, not for the one in flight).  The scale byte goes straight to the
+// encoded, not for the one in flight).  The input loads are non-temporal.  The scale byte goes straight to the
 // transposed scale tensor from lane 0 of each group: the 32 rows of a triple
 // are 32 consecutive bytes along M, written by one workgroup.
 #include <hip/hip_runtime.h>
@@ -77,6 +77,10 @@ __device__ __forceinline__ uint32_t triple_span(uint32_t rows, uint32_t K) {
     return rows ? (rows - 1) * K + uint32_t(QBLK) : 0u;
 }
 
+// Cache-policy operand of the input loads: nt (bit 1 on gfx950).  The codes
+// and scales are stored with the default policy, since the GEMM reads them next.
+constexpr int kLoadNT = 2;
+
 template <typename InT> struct InWords;      // 16-byte loads per lane per block
 template <> struct InWords<__bf16> { static constexpr int n = 1; };
 template <> struct InWords<float> { static constexpr int n = 2; };
@@ -124,9 +128,10 @@ __device__ __forceinline__ void fetch(u32x4 (&raw)[QU][InWords<InT>::n], const I
     for (int u = 0; u < QU; ++u) {
         const int d = u >> 1;
         const auto r = uniform_rsrc(x + it.base[d], triple_span(it.rows[d], K) * uint32_t(sizeof(InT)));
+        // non-temporal (cache policy nt): every input byte is read exactly once
 #pragma unroll
         for (int w = 0; w < InWords<InT>::n; ++w)
-            raw[u][w] = __builtin_amdgcn_raw_buffer_load_b128(r, ((u & 1) ? xo1 : xo0) + 16u * w, 0, 0);
+            raw[u][w] = __builtin_amdgcn_raw_buffer_load_b128(r, ((u & 1) ? xo1 : xo0) + 16u * w, 0, kLoadNT);
     }
 }
 
