@@ -62,29 +62,33 @@ bool ceil_e8m0(float amax, int* t) {
     return true;
 }
 
-// MX scale exponent for E4M3 elements: t = floor(log2(amax)) - 8, so the
-// scaled block's largest magnitude lies in [256, 512) (E4M3's top binade; the
-// values above 448 saturate).  frexp is exact for normal and subnormal amax.
-bool mx_floor_e8m0(float amax, int* t) {
+// MX scale exponent under the "Even" rounding of the third reference page
+// ("flydsl mxfp4 a4w4 MoE: bring gemm1/gemm2 to parity with the HIP backend",
+// section "Notes"): amax is first rounded to the element format's precision
+// (mbits fraction bits: 3 for E4M3, 1 for E2M1; nearest, ties to even), then
+// t = floor(log2(rounded amax)) - emax, emax being the exponent of the
+// format's largest power of two (8 for E4M3, 2 for E2M1).
+//
+// Read off the float's bit fields: amax = 1.f * 2^e.  Rounding 1.f to mbits
+// fraction bits reaches 2 exactly when the kept bits are all ones and the
+// dropped part is at least half a step (a tie rounds up there, since all ones
+// is odd), i.e. when the 23-bit fraction field is >= 2^23 - 2^(22 - mbits).
+// That carry adds one to the exponent.  Subnormal amax are normalized first
+// (their t lies far below the E8M0 range anyway).
+bool mx_even_e8m0(float amax, int mbits, int emax, int* t) {
     if (!(amax >= 0.0f) || std::isinf(amax)) return false;
     if (amax == 0.0f) { *t = 0; return true; }
-    int p;
-    std::frexp(amax, &p);                  // amax = f * 2^p, f in [0.5, 1): floor(log2) = p - 1
-    const int tt = p - 1 - 8;
-    if (tt < -127 || tt > 127) return false;
-    *t = tt;
-    return true;
-}
-
-// MXFP4 scale exponent: t = floor(log2(amax)) - 2 (E2M1's largest power of two
-// is 4), so the scaled block's largest magnitude lies in [4, 8); values above
-// 6 saturate.
-bool mx4_floor_e8m0(float amax, int* t) {
-    if (!(amax >= 0.0f) || std::isinf(amax)) return false;
-    if (amax == 0.0f) { *t = 0; return true; }
-    int p;
-    std::frexp(amax, &p);
-    const int tt = p - 1 - 2;
+    uint32_t u = f2u(amax);
+    int e = int(u >> 23) - 127;
+    uint32_t mant = u & 0x7FFFFFu;
+    if (e == -127) {                       // subnormal: normalize by hand
+        int p;
+        const float f = std::frexp(amax, &p);   // amax = f * 2^p, f in [0.5, 1)
+        e = p - 1;
+        mant = f2u(f * 2.0f) & 0x7FFFFFu;
+    }
+    const uint32_t carry_from = 0x800000u - (0x400000u >> mbits);
+    const int tt = e + (mant >= carry_from ? 1 : 0) - emax;
     if (tt < -127 || tt > 127) return false;
     *t = tt;
     return true;
@@ -238,7 +242,7 @@ extern "C" int fp8_quantize_mx_1x32(const float* x, int32_t G, int64_t R, int64_
                 nan |= row[k] != row[k];
             }
             int t;
-            if (nan || !mx_floor_e8m0(amax, &t)) { bad[size_t(gr)] = 1; return; }
+            if (nan || !mx_even_e8m0(amax, 3, 8, &t)) { bad[size_t(gr)] = 1; return; }
             scale_t[(g * KB + j) * R + r] = uint8_t(t + 127);
             for (int64_t k = 32 * j; k < 32 * j + 32; ++k) {
                 const float v = std::ldexp(row[k], -t);
@@ -278,7 +282,7 @@ extern "C" int fp4_quantize_mx_1x32(const float* x, int32_t G, int64_t R, int64_
                     nan |= row[k0 + i] != row[k0 + i];
                 }
                 int t;
-                if (nan || !mx4_floor_e8m0(amax, &t)) { bad[size_t(gr)] = 1; return; }
+                if (nan || !mx_even_e8m0(amax, 1, 2, &t)) { bad[size_t(gr)] = 1; return; }
                 scale_t[(g * KB + k0 / 32) * R + r] = uint8_t(t + 127);
                 for (int i = 0; i < 32; ++i) {
                     const float v = std::ldexp(row[k0 + i], -t);

@@ -168,8 +168,11 @@ GFG_API int grouped_mxfp8_gemm_masked(const void* a, const uint8_t* a_scale,
  * MX quantizer (CPU, synchronous) for the MXFP8 GEMM's operands:
  *   x [G][R][K] float -> q [G][R][K] e4m3, scale_t [G][K/32][R] E8M0
  * (A: G = 1, R = M; masked A: G groups of R = M_max; B: G experts of R = N).
- * Per row and 32-wide K block: t = floor(log2(max|x|)) - 8 (t = 0 for an
- * all-zero block), scale byte t + 127, q = E4M3(clamp(x / 2^t, -448, 448))
+ * Per row and 32-wide K block, the "Even" scale rounding of the third
+ * reference page ("flydsl mxfp4 a4w4 MoE: bring gemm1/gemm2 to parity with
+ * the HIP backend", section "Notes"): amax = max|x| is rounded to 3 fraction
+ * bits (nearest, ties to even), t = floor(log2(rounded amax)) - 8 (t = 0 for
+ * an all-zero block), scale byte t + 127, q = E4M3(clamp(x / 2^t, -448, 448))
  * nearest-even.  K must be a multiple of 32 (else GFG_EUNSUPPORTED);
  * GFG_ERANGE if t falls outside [-127, 127] or a value is not finite.
  */
@@ -238,8 +241,10 @@ GFG_API int grouped_mxfp4_gemm_silu_mul_masked(const void* a, const uint8_t* a_s
 /*
  * MXFP4 quantizer (CPU, synchronous):
  *   x [G][R][K] float -> q [G][R][K/2] (two E2M1 codes per byte), scale_t [G][K/32][R] E8M0.
- * Per row and 32-wide K block: t = floor(log2(max|x|)) - 2 (t = 0 for an
- * all-zero block), scale byte t + 127, code = E2M1(clamp(x / 2^t, -6, 6))
+ * Per row and 32-wide K block, the "Even" scale rounding at E2M1's precision:
+ * amax = max|x| rounded to 1 fraction bit (nearest, ties to even),
+ * t = floor(log2(rounded amax)) - 2 (t = 0 for an all-zero block), scale
+ * byte t + 127, code = E2M1(clamp(x / 2^t, -6, 6))
  * nearest-even (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 the sign).
  * Byte i of a row holds elements 2i (low nibble) and 2i + 1.  K must be a
  * multiple of 128 (else GFG_EUNSUPPORTED); GFG_ERANGE as fp8_quantize_mx_1x32.

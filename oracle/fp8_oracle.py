@@ -288,34 +288,53 @@ def grouped_gemm_silu_mul_masked(q_a, scale_a, q_b, scale_b, masked_m, out_init=
 
 
 # ---------------------------------------------------------------- MXFP8 (1 x 32 blocks)
-# The MX variant (third reference page: the MoE kernels there are "mxfp4
-# (a4w4)" with E8M0 scales under the rounding it calls "Even"; section
-# "Notes").  MX formats share one E8M0 scale per 32 consecutive elements along
+# The MX variant (third reference page, "[RadeonFlow] flydsl mxfp4 a4w4 MoE:
+# bring gemm1/gemm2 to parity with the HIP backend": the MoE kernels there are
+# "mxfp4 (a4w4)" with E8M0 scales under a rounding the section "Notes" calls
+# "Even").  MX formats share one E8M0 scale per 32 consecutive elements along
 # K, for activations and weights alike.  Readings of what the page leaves
 # open, for the FP8 (E4M3) element type:
-#   * the scale exponent is floor(log2(amax)) - 8, where 8 is the exponent of
-#     E4M3's largest power of two (256): the scaled block's largest magnitude
-#     lies in [256, 512);
-#   * elements are x / 2**t rounded to nearest, ties to even ("Even"), and
-#     clamped to +-448 (scaled values in (448, 512) saturate);
+#   * "Even" is a rounding of the scale: the block's amax is first rounded to
+#     the element format's precision (E4M3: 3 fraction bits), to nearest with
+#     ties to even, and the scale exponent is then
+#     t = floor(log2(rounded amax)) - 8, where 8 is the exponent of E4M3's
+#     largest power of two (256).  Without the rounding step this is the plain
+#     floor rule; with it, a block whose amax is within half an E4M3 step of
+#     the next power of two takes the larger scale;
+#   * elements are x / 2**t rounded to nearest, ties to even, and clamped to
+#     +-448 (scaled values in (448, 496) saturate);
 #   * an all-zero block gets t = 0 (byte 127); t outside [-127, 127] is an error;
 #   * both scale tensors are stored transposed, one row of bytes per 32-wide
 #     K block: ``[K/32, M]`` for A, ``[G, K/32, N]`` for B.
 
 MX_BLOCK = 32
 MX_EMAX = 8                # E4M3: largest power of two is 2**8
+MX_MBITS = 3               # E4M3 fraction bits
+
+
+def _even_scale_exponent(amax: np.ndarray, mbits: int, emax: int, name: str) -> np.ndarray:
+    """t = floor(log2(RNE(amax at mbits fraction bits))) - emax, exactly; 0 where amax == 0.
+
+    amax = f * 2**p with f in [0.5, 1) (frexp), so its significand is 2f in
+    [1, 2) and floor(log2(amax)) = p - 1.  2f * 2**mbits is exact in float64;
+    rounding it to an integer (numpy's rint: nearest, ties to even) rounds the
+    significand to mbits fraction bits, and the result reaches 2 * 2**mbits
+    exactly when the rounding carries into the next power of two.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    if np.any(~np.isfinite(amax)) or np.any(amax < 0):
+        raise ValueError(f"{name}: amax must be finite and >= 0")
+    f, p = np.frexp(np.where(amax > 0, amax, 1.0))
+    carry = np.rint(2.0 * f * 2.0 ** mbits) >= 2.0 ** (mbits + 1)
+    t = np.where(amax > 0, p.astype(np.int64) - 1 + carry.astype(np.int64) - emax, 0)
+    if np.any(t < -127) or np.any(t > 127):
+        raise ValueError(f"{name}: scale outside the E8M0 range")
+    return t
 
 
 def mx_exponent(amax: np.ndarray) -> np.ndarray:
-    """t = floor(log2(amax)) - 8 exactly (frexp), 0 where amax == 0."""
-    amax = np.asarray(amax, dtype=np.float64)
-    if np.any(~np.isfinite(amax)) or np.any(amax < 0):
-        raise ValueError("mx_exponent: amax must be finite and >= 0")
-    _, p = np.frexp(np.where(amax > 0, amax, 1.0))     # amax = f * 2**p, f in [0.5, 1)
-    t = np.where(amax > 0, p.astype(np.int64) - 1 - MX_EMAX, 0)
-    if np.any(t < -127) or np.any(t > 127):
-        raise ValueError("mx_exponent: scale outside the E8M0 range")
-    return t
+    """E4M3 MX scale exponent under the "Even" rule (3 fraction bits, emax 8)."""
+    return _even_scale_exponent(amax, MX_MBITS, MX_EMAX, "mx_exponent")
 
 
 def quantize_mx_1x32(x: np.ndarray):
@@ -380,14 +399,20 @@ def grouped_gemm_mx_masked(q_a, scale_a, q_b, scale_b, masked_m, d_init=None):
 # "Summary").  E2M1 (OCP FP4): 1 sign, 2 exponent bits (bias 1), 1 mantissa
 # bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinity or NaN.  Readings
 # of what the page leaves open:
-#   * scale exponent t = floor(log2(amax)) - 2 (2 is the exponent of E2M1's
-#     largest power of two, 4); elements x / 2**t rounded to nearest, ties to
-#     the even code ("Even"), clamped to +-6; all-zero block t = 0;
+#   * the scale follows the same "Even" rule as MXFP8 at E2M1's precision:
+#     amax rounded to 1 fraction bit (nearest, ties to even), then
+#     t = floor(log2(rounded amax)) - 2 (2 is the exponent of E2M1's largest
+#     power of two, 4), so a block whose amax significand is at least 1.75
+#     takes the larger scale and its largest element never lies above 7
+#     after scaling;
+#   * elements x / 2**t rounded to nearest, ties to the even code, clamped to
+#     +-6; all-zero block t = 0;
 #   * two elements per byte, the lower K index in the low nibble;
 #   * scales as for MXFP8: [K/32, M] for A and [G, K/32, N] for B.
 
 E2M1_MAX = 6.0
 MX4_EMAX = 2
+MX4_MBITS = 1              # E2M1 fraction bits
 
 
 def decode_e2m1(codes: np.ndarray) -> np.ndarray:
@@ -419,15 +444,8 @@ def encode_e2m1_rne(x: np.ndarray) -> np.ndarray:
 
 
 def mx4_exponent(amax: np.ndarray) -> np.ndarray:
-    """t = floor(log2(amax)) - 2 exactly, 0 where amax == 0."""
-    amax = np.asarray(amax, dtype=np.float64)
-    if np.any(~np.isfinite(amax)) or np.any(amax < 0):
-        raise ValueError("mx4_exponent: amax must be finite and >= 0")
-    _, p = np.frexp(np.where(amax > 0, amax, 1.0))
-    t = np.where(amax > 0, p.astype(np.int64) - 1 - MX4_EMAX, 0)
-    if np.any(t < -127) or np.any(t > 127):
-        raise ValueError("mx4_exponent: scale outside the E8M0 range")
-    return t
+    """E2M1 MX scale exponent under the "Even" rule (1 fraction bit, emax 2)."""
+    return _even_scale_exponent(amax, MX4_MBITS, MX4_EMAX, "mx4_exponent")
 
 
 def quantize_mx4_1x32(x: np.ndarray):

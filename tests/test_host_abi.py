@@ -222,12 +222,16 @@ def test_mx_quantizer_bit_exact(shape):
 
 
 def test_mx_quantizer_boundaries_bit_exact():
-    """Blocks at the exponent edges (amax = 256*2^t, one ulp below, 512*2^t),
-    saturating blocks (scaled maximum in (448, 512)), subnormal elements, an
-    all-zero block and negative zeros."""
+    """Blocks at the exponent edges (amax = 256*2^t and one float32 ulp
+    below), at the "Even" carry point (amax = 496*2^t, the tie that rounds up
+    to 512*2^t, and one ulp below, which does not), saturating blocks (scaled
+    maximum in (448, 496)), subnormal elements, an all-zero block and negative
+    zeros."""
+    f32_below = lambda v: float(np.nextafter(np.float32(v), np.float32(0)))
     blocks = []
     for t in (-30, -1, 0, 5, 60):
-        for amax in (256.0 * 2.0 ** t, np.nextafter(256.0 * 2.0 ** t, 0), 500.0 * 2.0 ** t, 448.0 * 2.0 ** t):
+        for amax in (256.0 * 2.0 ** t, f32_below(256.0 * 2.0 ** t), 496.0 * 2.0 ** t, f32_below(496.0 * 2.0 ** t),
+                     500.0 * 2.0 ** t, 480.0 * 2.0 ** t, 448.0 * 2.0 ** t):
             b = np.linspace(-1, 1, 32) * amax
             b[7] = amax
             blocks.append(b)
@@ -300,18 +304,21 @@ def test_mx4_quantizer_bit_exact(shape):
 
 
 def test_mx4_quantizer_boundaries_bit_exact():
-    """Exponent edges (amax = 4*2^t, one ulp below, 8*2^t), saturating blocks
-    (scaled maximum in (6, 8)), every E2M1 midpoint, an all-zero block and
-    negative zeros."""
+    """Exponent edges (amax = 4*2^t and one float32 ulp below), the "Even"
+    carry point (amax = 7*2^t, the tie that rounds up to 8*2^t, and one ulp
+    below), saturating blocks (scaled maximum in (6, 7)), every E2M1 midpoint,
+    an all-zero block and negative zeros."""
+    f32_below = lambda v: float(np.nextafter(np.float32(v), np.float32(0)))
     blocks = []
     for t in (-30, -1, 0, 5, 60):
-        for amax in (4.0 * 2.0 ** t, np.nextafter(4.0 * 2.0 ** t, 0), 7.5 * 2.0 ** t, 6.0 * 2.0 ** t):
+        for amax in (4.0 * 2.0 ** t, f32_below(4.0 * 2.0 ** t), 7.0 * 2.0 ** t, f32_below(7.0 * 2.0 ** t),
+                     7.5 * 2.0 ** t, 6.5 * 2.0 ** t, 6.0 * 2.0 ** t):
             b = np.linspace(-1, 1, 32) * amax
             b[9] = amax
             blocks.append(b)
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
     b = np.concatenate([mids, -mids, mids * 0.999, mids * 1.001])
-    blocks.append(b)                        # amax 6.006: t = 0, the 1.001 * 6 saturates
+    blocks.append(b)                        # amax 6.006 = 1.5015 * 4: t = 0, the 1.001 * 6 saturates
     z = np.zeros(32)
     z[5] = -0.0
     blocks.append(z)

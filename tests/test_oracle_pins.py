@@ -20,13 +20,13 @@ from fp8_block_scaled_amd import workloads as wl
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _read_golden(name):
+def _read_golden(name, cols=2):
     rows = []
     with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.split("#", 1)[0].strip()
             if line:
-                rows.append(line.split()[:2])
+                rows.append(line.split()[:cols])
     return rows
 
 
@@ -556,28 +556,53 @@ def test_silu_mul_pins_catch_planted_mistakes(monkeypatch):
 
 
 # ------------------------------------------------------------------ MXFP8 (1 x 32) pins
+def _bf_even_exponent(a: float, mbits: int, emax: int) -> int:
+    """The "Even" scale exponent by brute force: the nearest value with mbits
+    fraction bits, found by trying every candidate j * 2**(e - mbits) of a's
+    binade [2**e, 2**(e+1)] (ties to the even j), then the integer t with
+    2**(t + emax) <= that value < 2**(t + emax + 1) by linear search."""
+    if a == 0:
+        return 0
+    e = next(k for k in range(-200, 200) if 2.0 ** k <= a < 2.0 ** (k + 1))
+    step = 2.0 ** (e - mbits)
+    best = min((abs(j * step - a), j % 2, j * step) for j in range(2 ** mbits, 2 ** (mbits + 1) + 1))[2]
+    return next(k for k in range(-200, 200) if 2.0 ** k <= best < 2.0 ** (k + 1)) - emax
+
+
 def test_mx_exponent_golden():
-    rows = _read_golden("mx_e8m0_floor.txt")
-    amax = np.array([float(a) for a, _ in rows])
-    want = np.array([int(b) for _, b in rows])
+    """E4M3 column of the hand-derived "Even" table."""
+    rows = _read_golden("mx_e8m0_even.txt", cols=3)
+    amax = np.array([float(a) for a, _, _ in rows])
+    want = np.array([int(b) for _, b, _ in rows])
     assert np.array_equal(o.mx_exponent(amax) + 127, want)
 
 
 def test_mx_exponent_bruteforce():
     rng = np.random.default_rng(31)
-    amax = np.concatenate([rng.uniform(0, 1, 500) * 10.0 ** rng.uniform(-30, 30, 500),
-                           2.0 ** rng.integers(-100, 100, 50).astype(np.float64),
-                           np.nextafter(2.0 ** rng.integers(-100, 100, 50).astype(np.float64), 0)])
+    p2 = 2.0 ** rng.integers(-100, 100, 50).astype(np.float64)
+    amax = np.concatenate([rng.uniform(0, 1, 500) * 10.0 ** rng.uniform(-30, 30, 500), p2, np.nextafter(p2, 0),
+                           p2 * 1.9375, np.nextafter(p2 * 1.9375, 0), p2 * 1.96875, p2 * 1.875])
     t = o.mx_exponent(amax)
     for a, ti in zip(amax, t):
-        want = next(k for k in range(-140, 140) if 256.0 * 2.0 ** k <= a < 512.0 * 2.0 ** k)
+        want = _bf_even_exponent(float(a), 3, 8)
         assert ti == want, (a, ti, want)
     with pytest.raises(ValueError):
         o.mx_exponent(np.array([1e-37]))            # t = -131: below E8M0's range
 
 
+def test_mx_even_scale_bounds_the_scaled_block():
+    """What the "Even" rounding buys: the scaled block maximum stays below the
+    midpoint above the format's top power of two (E4M3: 496 = 1.9375 * 256;
+    E2M1: 7 = 1.75 * 4), and at or above half that power's binade."""
+    rng = np.random.default_rng(35)
+    amax = rng.uniform(0, 1, 2000) * 10.0 ** rng.uniform(-20, 20, 2000)
+    for fn, hi, lo in ((o.mx_exponent, 496.0, 128.0), (o.mx4_exponent, 7.0, 2.0)):
+        v = amax / np.exp2(fn(amax).astype(np.float64))
+        assert np.all(v < hi) and np.all(v >= lo)
+
+
 def _bf_quant_mx(x):
-    """Per row, per 32-wide block: brute-force exponent search, clamp, exhaustive RNE encode."""
+    """Per row, per 32-wide block: brute-force "Even" exponent, clamp, exhaustive RNE encode."""
     R, K = x.shape
     q = np.zeros((R, K), np.uint8)
     s = np.zeros((K // 32, R), np.uint8)
@@ -585,7 +610,7 @@ def _bf_quant_mx(x):
         for j in range(K // 32):
             blk = [float(v) for v in x[r, 32 * j:32 * j + 32]]
             amax = max(abs(v) for v in blk)
-            t = 0 if amax == 0 else next(k for k in range(-140, 140) if 256.0 * 2.0 ** k <= amax < 512.0 * 2.0 ** k)
+            t = _bf_even_exponent(amax, 3, 8)
             s[j, r] = t + 127
             for i, v in enumerate(blk):
                 q[r, 32 * j + i] = _bf_encode(min(max(v / 2.0 ** t, -448.0), 448.0))
@@ -593,20 +618,25 @@ def _bf_quant_mx(x):
 
 
 def test_mx_quantizer_bruteforce_tiny():
-    """Ragged magnitudes, an all-zero block, and blocks whose scaled maximum
-    lies in (448, 512) (saturating to +-448)."""
+    """Ragged magnitudes, an all-zero block, blocks whose scaled maximum lies
+    in (448, 496) (saturating to +-448), and a block whose amax rounds up to
+    the next power of two (the larger scale, no saturation)."""
     rng = np.random.default_rng(32)
     x = (rng.standard_normal((5, 128)) * 10.0 ** rng.uniform(-3, 3, (5, 1))).astype(np.float32)
     x[1, 32:64] = 0.0
-    x[2, 64:96] = rng.uniform(-1, 1, 32).astype(np.float32) * 8.0
-    x[2, 70] = 7.75            # t = -6: scaled maximum 7.75 * 64 = 496, saturates to 448
-    x[3, 0:32] = np.float32(500.0)
-    x[3, 5] = np.float32(-470.0)
+    x[2, 64:96] = rng.uniform(-1, 1, 32).astype(np.float32) * 7.0
+    x[2, 70] = 7.5             # 1.875 * 4: t = -6, scaled 480, saturates to 448
+    x[3, 0:32] = np.float32(460.0)
+    x[3, 5] = np.float32(-470.0)   # amax 470 = 1.836 * 256: t = 0, +-460/470 saturate to +-448
+    x[4, 96:128] = np.float32(1.0)
+    x[4, 100] = np.float32(-7.75)  # 1.9375 * 4 rounds to 8: t = -5, -7.75 * 32 = -248 -> -256
     q, s = o.quantize_mx_1x32(x)
     bq, bs = _bf_quant_mx(x)
     assert np.array_equal(s, bs)
     assert np.array_equal(q, bq)
+    assert q[2, 70] == 0x7E                               # saturated to 448
     assert q[3, 0] == 0x7E and q[3, 5] == 0xFE           # saturated to +-448
+    assert s[3, 4] == 122 and q[4, 100] == 0xF8          # t = -5; -256 = -(2^8)
 
 
 def _bf_mx_gemm_rows(qa, sa, qb, sb, rows_a, g):
@@ -656,8 +686,9 @@ def test_mx_masked_gemm_bruteforce_tiny():
 
 def test_mx_pins_catch_planted_mistakes(monkeypatch):
     """Plant plausible MX mistakes in the oracle (on the CPU): the ceil rule of
-    the (1,128) path instead of floor, scales applied per 128 instead of per
-    32, and no saturation before encoding."""
+    the (1,128) path instead of "Even", the plain floor rule (no rounding of
+    amax) instead of "Even", scales applied per 128 instead of per 32, and no
+    saturation before encoding."""
     failures = 0
     real_exp = o.mx_exponent
     monkeypatch.setattr(o, "mx_exponent", lambda a: o.e8m0_ceil_exponent(a))
@@ -665,6 +696,17 @@ def test_mx_pins_catch_planted_mistakes(monkeypatch):
         test_mx_exponent_golden()
     except AssertionError:
         failures += 1
+
+    def floor_rule(a):
+        a = np.asarray(a, np.float64)
+        _, p = np.frexp(np.where(a > 0, a, 1.0))
+        return np.where(a > 0, p.astype(np.int64) - 1 - 8, 0)
+    monkeypatch.setattr(o, "mx_exponent", floor_rule)
+    for pin in (test_mx_exponent_golden, test_mx_quantizer_bruteforce_tiny):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
     monkeypatch.setattr(o, "mx_exponent", real_exp)
     real_dq = o.dequantize_mx
 
@@ -684,7 +726,7 @@ def test_mx_pins_catch_planted_mistakes(monkeypatch):
     except (AssertionError, ValueError):
         failures += 1
     monkeypatch.setattr(o.np, "clip", real_clip)
-    assert failures == 3
+    assert failures == 5
 
 
 # ------------------------------------------------------------------ MXFP4 (E2M1) pins
@@ -722,13 +764,23 @@ def test_e2m1_encode_bruteforce():
         o.encode_e2m1_rne(np.array([6.5]))
 
 
+def test_mx4_exponent_golden():
+    """E2M1 column of the hand-derived "Even" table."""
+    rows = _read_golden("mx_e8m0_even.txt", cols=3)
+    amax = np.array([float(a) for a, _, _ in rows])
+    want = np.array([int(c) for _, _, c in rows])
+    assert np.array_equal(o.mx4_exponent(amax) + 127, want)
+
+
 def test_mx4_exponent_bruteforce():
     rng = np.random.default_rng(52)
-    amax = np.concatenate([rng.uniform(0, 1, 400) * 10.0 ** rng.uniform(-30, 30, 400),
-                           2.0 ** rng.integers(-100, 100, 40).astype(np.float64), np.array([0.0, 4.0, 7.999, 8.0])])
+    p2 = 2.0 ** rng.integers(-100, 100, 40).astype(np.float64)
+    amax = np.concatenate([rng.uniform(0, 1, 400) * 10.0 ** rng.uniform(-30, 30, 400), p2, p2 * 1.75,
+                           np.nextafter(p2 * 1.75, 0), p2 * 1.5, p2 * 1.25,
+                           np.array([0.0, 4.0, 6.0, 6.999, 7.0, 7.999, 8.0])])
     t = o.mx4_exponent(amax)
     for a, ti in zip(amax, t):
-        want = 0 if a == 0 else next(k for k in range(-140, 140) if 4.0 * 2.0 ** k <= a < 8.0 * 2.0 ** k)
+        want = _bf_even_exponent(float(a), 1, 2)
         assert ti == want, (a, ti, want)
 
 
@@ -740,7 +792,7 @@ def _bf_quant_mx4(x):
         for j in range(K // 32):
             blk = [float(v) for v in x[r, 32 * j:32 * j + 32]]
             amax = max(abs(v) for v in blk)
-            t = 0 if amax == 0 else next(k for k in range(-140, 140) if 4.0 * 2.0 ** k <= amax < 8.0 * 2.0 ** k)
+            t = _bf_even_exponent(amax, 1, 2)
             s[j, r] = t + 127
             for i, v in enumerate(blk):
                 k = 32 * j + i
@@ -753,12 +805,15 @@ def test_mx4_quantizer_bruteforce_tiny():
     rng = np.random.default_rng(53)
     x = (rng.standard_normal((4, 96)) * 10.0 ** rng.uniform(-3, 3, (4, 1))).astype(np.float32)
     x[1, 32:64] = 0.0
-    x[2, 0:32] = np.float32(7.5)        # t = 0 (4 <= 7.5 < 8): 7.5 saturates to 6
-    x[2, 3] = np.float32(-7.0)
+    x[2, 0:32] = np.float32(6.5)        # amax 6.8 = 1.7 * 4: t = 0, 6.5 saturates to 6
+    x[2, 3] = np.float32(-6.8)
+    x[3, 64:96] = np.float32(0.5)
+    x[3, 70] = np.float32(7.0)          # 1.75 * 4 rounds to 8: t = 1; 7 / 2 = 3.5 -> 4 (tie, even code)
     q, s = o.quantize_mx4_1x32(x)
     bq, bs = _bf_quant_mx4(x)
     assert np.array_equal(s, bs) and np.array_equal(q, bq)
     assert q[2, 0] == 0x77 and (q[2, 1] >> 4) == 0xF
+    assert s[2, 3] == 128 and (q[3, 35] & 15) == 6      # code 6 = 4.0
 
 
 def test_mx4_dequantize_nibble_order():
@@ -821,7 +876,8 @@ def test_mx4_masked_gemm_bruteforce_tiny():
 
 def test_mx4_pins_catch_planted_mistakes(monkeypatch):
     """Planted MXFP4 mistakes (on the CPU): nibbles in the wrong order, the
-    FP8 exponent rule (-8) instead of FP4's (-2), and no saturation."""
+    FP8 exponent rule instead of FP4's, the plain floor rule (no rounding of
+    amax) instead of "Even", and no saturation."""
     failures = 0
     real_dq = o.dequantize_mx4
 
@@ -840,6 +896,17 @@ def test_mx4_pins_catch_planted_mistakes(monkeypatch):
         test_mx4_exponent_bruteforce()
     except AssertionError:
         failures += 1
+
+    def floor_rule(a):
+        a = np.asarray(a, np.float64)
+        _, p = np.frexp(np.where(a > 0, a, 1.0))
+        return np.where(a > 0, p.astype(np.int64) - 1 - 2, 0)
+    monkeypatch.setattr(o, "mx4_exponent", floor_rule)
+    for pin in (test_mx4_exponent_golden, test_mx4_quantizer_bruteforce_tiny):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
     monkeypatch.setattr(o, "mx4_exponent", real_exp)
     real_clip = np.clip
     monkeypatch.setattr(o.np, "clip", lambda v, lo, hi: v)
@@ -848,7 +915,7 @@ def test_mx4_pins_catch_planted_mistakes(monkeypatch):
     except (AssertionError, ValueError):
         failures += 1
     monkeypatch.setattr(o.np, "clip", real_clip)
-    assert failures == 3
+    assert failures == 5
 
 
 # ------------------------------------------------------------------ a4w4 gemm1 with silu_mul pins
