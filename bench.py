@@ -264,7 +264,7 @@ def bench_quant(args):
     def step(i):
         rc = gfg.raw_quantize_act_device(*calls[i % nsets])
         if rc:
-            raise gfg.GfgError(rc, gfg.load_library().gfg_last_error().decode())
+            raise gfg.GfgError(rc, gfg.load_library().grouped_fp8_last_error().decode())
 
     for i in range(args.warmup):
         step(i)
@@ -416,7 +416,7 @@ def main():
         fn, a = calls[i % len(calls)]
         rc = fn(*a)
         if rc:
-            raise gfg.GfgError(rc, gfg.load_library().gfg_last_error().decode())
+            raise gfg.GfgError(rc, gfg.load_library().grouped_fp8_last_error().decode())
 
     for i in range(args.warmup):
         step(i)

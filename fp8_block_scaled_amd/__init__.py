@@ -36,7 +36,9 @@ __all__ = [
     "OUT_BF16", "OUT_F16", "IN_F32", "IN_BF16",
 ]
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgfg.so")
+# GFG_LIBRARY names another build of the library to load (the host-sanitizer
+# build of the CPU tests); by default the in-tree libgfg.so.
+_LIB_PATH = os.environ.get("GFG_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgfg.so")
 OUT_BF16, OUT_F16 = 0, 1
 IN_F32, IN_BF16 = 0, 1
 _STATUS = {0: "GFG_OK", 1: "GFG_EINVAL", 2: "GFG_EUNSUPPORTED", 3: "GFG_EHIP", 4: "GFG_ERANGE"}
@@ -89,8 +91,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_quantize_weight_128x128.restype = ctypes.c_int
     lib.fp8_quantize_act_1x128_device.argtypes = [vp, i32, i32, i64, i64, vp, vp, vp]
     lib.fp8_quantize_act_1x128_device.restype = ctypes.c_int
-    lib.gfg_last_error.argtypes = []
-    lib.gfg_last_error.restype = ctypes.c_char_p
+    lib.grouped_fp8_last_error.argtypes = []
+    lib.grouped_fp8_last_error.restype = ctypes.c_char_p
     lib.gfg_version.argtypes = []
     lib.gfg_version.restype = ctypes.c_char_p
     if path is None:
@@ -100,7 +102,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 
 def _check(rc: int):
     if rc != 0:
-        raise GfgError(rc, load_library().gfg_last_error().decode())
+        raise GfgError(rc, load_library().grouped_fp8_last_error().decode())
 
 
 # ------------------------------------------------------------------ raw pointer calls

@@ -57,5 +57,50 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host sanitizers for the CPU tests: AddressSanitizer and UndefinedBehavior-
+# Sanitizer on the host code only (the device code is built as usual), with
+# clang's runtime, which the test process preloads.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared AddressSanitizer runtime (to preload)."""
+    clang = "/opt/rocm/llvm/bin/clang++"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.exists(path):
+        raise RuntimeError("clang's AddressSanitizer runtime was not found")
+    return path
+
+
+def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """Build the library with ASan + UBSan on its host code into out_dir;
+    returns the path of the .so (load it with GFG_LIBRARY and the runtime of
+    asan_runtime() preloaded)."""
+    hipcc = _hipcc()
+    clang = "/opt/rocm/llvm/bin/clang++"
+    os.makedirs(out_dir, exist_ok=True)
+    common = ["-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
+    o = lambda n: os.path.join(out_dir, n)
+    steps = [
+        [hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops", "-c", os.path.join(CSRC, "gfg_gemm.hip"), "-o", o("gfg_gemm.o")],
+        [hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops", "-c", os.path.join(CSRC, "gfg_quant.hip"), "-o", o("gfg_quant.o")],
+        [clang, *common, "-pthread", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-c",
+         os.path.join(CSRC, "gfg_host.cpp"), "-o", o("gfg_host.o")],
+        [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *SAN_HOST[:4], "-shared-libasan",
+         o("gfg_gemm.o"), o("gfg_quant.o"), o("gfg_host.o"), "-o", o("libgfg_san.so")],
+    ]
+    for cmd in steps:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return o("libgfg_san.so")
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -828,6 +828,23 @@ int check_common(const char* fn, const void* a, const void* sa, const void* b, c
     if (N > (int64_t(1) << 30) || K > (int64_t(1) << 23))   // 32-bit in-tile offsets
         return fail(GFG_EUNSUPPORTED, "%s: N=%lld or K=%lld too large (N <= 2^30, K <= 2^23)", fn,
                     (long long)N, (long long)K);
+    // B rows are addressed from the tile's first row with 32-bit byte offsets
+    // (the up rows of silu_mul lie up to N/2 + 255 rows further on), and the
+    // MX B scales [K/32][N] of an expert with 32-bit buffer offsets
+    if (N * K >= (int64_t(1) << 32))
+        return fail(GFG_EUNSUPPORTED, "%s: N*K=%lld bytes of one expert's B must stay below 2^32", fn,
+                    (long long)(N * K));
+    return GFG_OK;
+}
+
+// The A-scale region [scale blocks along K][rows] is read with 32-bit buffer
+// offsets.  sk = scale blocks per 128 bytes of a row: 1 for the (1,128) scales,
+// 4 for MXFP8, 8 for MXFP4 (K counts bytes here).
+int check_scale_extent(const char* fn, int64_t rows, int64_t K, int sk) {
+    const int64_t extent = rows * (K / 128) * sk;
+    if (extent >= (int64_t(1) << 32))
+        return fail(GFG_EUNSUPPORTED, "%s: the A-scale region (%lld bytes) must stay below 2^32", fn,
+                    (long long)extent);
     return GFG_OK;
 }
 
@@ -837,9 +854,10 @@ int group_m_default() { return 4; }
 // grouped_layout, B [G][N][K].  Returns GFG_OK with *n_cand set, or an error.
 int contig_params(const char* fn, const void* a, const uint8_t* a_scale, const void* b, const uint8_t* b_scale,
                   const int32_t* grouped_layout, void* d, int64_t M, int64_t N, int64_t K, int32_t G,
-                  int32_t out_dtype, Params* p, int64_t* n_cand) {
+                  int32_t out_dtype, int sk, Params* p, int64_t* n_cand) {
     if (M < 0) return fail(GFG_EINVAL, "%s: M=%lld is negative", fn, (long long)M);
     if (int rc = check_common(fn, a, a_scale, b, b_scale, grouped_layout, d, N, K, G, out_dtype)) return rc;
+    if (int rc = check_scale_extent(fn, M, K, sk)) return rc;
     *n_cand = (M + BM - 1) / BM;
     if (*n_cand > MT_MAX)
         return fail(GFG_EUNSUPPORTED, "%s: M=%lld exceeds %d rows", fn, (long long)M, MT_MAX * BM);
@@ -863,9 +881,10 @@ int contig_params(const char* fn, const void* a, const uint8_t* a_scale, const v
 // Parameters of a masked call: A [G][M_max][K], rows m < masked_m[g] computed.
 int masked_params(const char* fn, const void* a, const uint8_t* a_scale, const void* b, const uint8_t* b_scale,
                   const int32_t* masked_m, void* d, int32_t G, int64_t M_max, int64_t N, int64_t K,
-                  int32_t out_dtype, Params* p, int64_t* n_cand) {
+                  int32_t out_dtype, int sk, Params* p, int64_t* n_cand) {
     if (M_max < 0) return fail(GFG_EINVAL, "%s: M_max=%lld is negative", fn, (long long)M_max);
     if (int rc = check_common(fn, a, a_scale, b, b_scale, masked_m, d, N, K, G, out_dtype)) return rc;
+    if (int rc = check_scale_extent(fn, M_max, K, sk)) return rc;
     const int64_t per = (M_max + BM - 1) / BM;
     *n_cand = per * G;
     if (*n_cand > MT_MAX)
@@ -940,7 +959,7 @@ extern "C" int grouped_fp8_gemm_contiguous(const void* a, const uint8_t* a_scale
     Params p;
     int64_t n_cand = 0;
     if (int rc = contig_params("grouped_fp8_gemm_contiguous", a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G,
-                               out_dtype, &p, &n_cand))
+                               out_dtype, 1, &p, &n_cand))
         return rc;
     if (M == 0) return GFG_OK;
     return dispatch<false>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
@@ -953,7 +972,7 @@ extern "C" int grouped_fp8_gemm_masked(const void* a, const uint8_t* a_scale, co
     Params p;
     int64_t n_cand = 0;
     if (int rc = masked_params("grouped_fp8_gemm_masked", a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K,
-                               out_dtype, &p, &n_cand))
+                               out_dtype, 1, &p, &n_cand))
         return rc;
     if (M_max == 0) return GFG_OK;
     return dispatch<true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
@@ -968,7 +987,7 @@ extern "C" int grouped_fp8_gemm_silu_mul_contiguous(const void* a, const uint8_t
     if (int rc = check_silu(fn, I, M < 0 ? 0 : M, a_scale)) return rc;
     Params p;
     int64_t n_cand = 0;
-    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, 2 * I, K, G, out_dtype, &p, &n_cand))
+    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, 2 * I, K, G, out_dtype, 1, &p, &n_cand))
         return rc;
     if (M == 0) return GFG_OK;
     return dispatch_silu<false>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
@@ -983,7 +1002,7 @@ extern "C" int grouped_fp8_gemm_silu_mul_masked(const void* a, const uint8_t* a_
     if (int rc = check_silu(fn, I, M_max < 0 ? 0 : M_max, a_scale)) return rc;
     Params p;
     int64_t n_cand = 0;
-    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, 2 * I, K, out_dtype, &p, &n_cand))
+    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, 2 * I, K, out_dtype, 1, &p, &n_cand))
         return rc;
     if (M_max == 0) return GFG_OK;
     return dispatch_silu<true>(p, unsigned(n_cand), out_dtype, static_cast<hipStream_t>(stream));
@@ -997,7 +1016,7 @@ extern "C" int grouped_mxfp8_gemm_contiguous(const void* a, const uint8_t* a_sca
     const char* fn = "grouped_mxfp8_gemm_contiguous";
     Params p;
     int64_t n_cand = 0;
-    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out_dtype, &p, &n_cand))
+    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, N, K, G, out_dtype, 4, &p, &n_cand))
         return rc;
     if (int rc = check_mx(fn, N, M, a_scale, b_scale)) return rc;
     if (M == 0) return GFG_OK;
@@ -1011,7 +1030,7 @@ extern "C" int grouped_mxfp8_gemm_masked(const void* a, const uint8_t* a_scale, 
     const char* fn = "grouped_mxfp8_gemm_masked";
     Params p;
     int64_t n_cand = 0;
-    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, &p, &n_cand))
+    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K, out_dtype, 4, &p, &n_cand))
         return rc;
     if (int rc = check_mx(fn, N, M_max, a_scale, b_scale)) return rc;
     if (M_max == 0) return GFG_OK;
@@ -1036,7 +1055,7 @@ extern "C" int grouped_mxfp4_gemm_contiguous(const void* a, const uint8_t* a_sca
     if (int rc = check_k4(fn, K)) return rc;
     Params p;
     int64_t n_cand = 0;
-    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, N, K / 2, G, out_dtype, &p, &n_cand))
+    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, N, K / 2, G, out_dtype, 8, &p, &n_cand))
         return rc;
     if (int rc = check_mx(fn, N, M, a_scale, b_scale)) return rc;
     if (M == 0) return GFG_OK;
@@ -1051,7 +1070,7 @@ extern "C" int grouped_mxfp4_gemm_masked(const void* a, const uint8_t* a_scale, 
     if (int rc = check_k4(fn, K)) return rc;
     Params p;
     int64_t n_cand = 0;
-    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K / 2, out_dtype, &p, &n_cand))
+    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, N, K / 2, out_dtype, 8, &p, &n_cand))
         return rc;
     if (int rc = check_mx(fn, N, M_max, a_scale, b_scale)) return rc;
     if (M_max == 0) return GFG_OK;
@@ -1071,7 +1090,7 @@ extern "C" int grouped_mxfp4_gemm_silu_mul_contiguous(const void* a, const uint8
     if (int rc = check_silu(fn, I, M < 0 ? 0 : M, a_scale)) return rc;
     Params p;
     int64_t n_cand = 0;
-    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, 2 * I, K / 2, G, out_dtype, &p,
+    if (int rc = contig_params(fn, a, a_scale, b, b_scale, grouped_layout, d, M, 2 * I, K / 2, G, out_dtype, 8, &p,
                                &n_cand))
         return rc;
     if (int rc = check_mx(fn, 2 * I, M, a_scale, b_scale)) return rc;
@@ -1089,7 +1108,7 @@ extern "C" int grouped_mxfp4_gemm_silu_mul_masked(const void* a, const uint8_t* 
     if (int rc = check_silu(fn, I, M_max < 0 ? 0 : M_max, a_scale)) return rc;
     Params p;
     int64_t n_cand = 0;
-    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, 2 * I, K / 2, out_dtype, &p,
+    if (int rc = masked_params(fn, a, a_scale, b, b_scale, masked_m, d, G, M_max, 2 * I, K / 2, out_dtype, 8, &p,
                                &n_cand))
         return rc;
     if (int rc = check_mx(fn, 2 * I, M_max, a_scale, b_scale)) return rc;

@@ -147,7 +147,7 @@ void parallel_for(int64_t n, F&& f) {
 
 using namespace gfg;
 
-extern "C" const char* gfg_last_error(void) { return t_last_error.c_str(); }
+extern "C" const char* grouped_fp8_last_error(void) { return t_last_error.c_str(); }
 
 extern "C" const char* gfg_version(void) { return "gfg 0.1 gfx950"; }
 

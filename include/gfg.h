@@ -23,7 +23,7 @@
  *  - Quantizer pointers are HOST pointers owned by the caller; the quantizers
  *    are synchronous CPU functions.
  *  - Return value: GFG_OK (0) or an error code; no exceptions cross the ABI.
- *    gfg_last_error() returns a thread-local message for the last failure on
+ *    grouped_fp8_last_error() returns a thread-local message for the last failure on
  *    the calling thread (valid until that thread's next call).
  *  - Argument checks (null pointers, sizes, enum values) happen on the host
  *    before anything is launched.  Device-resident metadata cannot be
@@ -76,7 +76,11 @@ enum gfg_in_dtype { GFG_IN_F32 = 0, GFG_IN_BF16 = 1 };
  *
  * Sizes: M >= 0 (M = 0 is a no-op), N > 0 and K > 0 multiples of 128 with
  * N <= 2^30 and K <= 2^23 (else GFG_EUNSUPPORTED), 1 <= G <= 65535, ceil(M/128) <= 4096 (else
- * GFG_EUNSUPPORTED).
+ * GFG_EUNSUPPORTED).  The kernels address one expert's B and the A-scale
+ * tensor with 32-bit byte offsets: N*K (bytes of one expert's B) and the
+ * scale tensor's bytes (here ceil(K/128)*M; for the MX GEMMs below, one
+ * byte per 32 K elements of every row) must stay below 2^32, else
+ * GFG_EUNSUPPORTED.  These bounds hold for every entry point below.
  */
 GFG_API int grouped_fp8_gemm_contiguous(const void* a, const uint8_t* a_scale,
                                 const void* b, const uint8_t* b_scale,
@@ -297,7 +301,7 @@ GFG_API int fp8_quantize_act_1x128_device(const void* x, int32_t in_dtype, int32
                                           uint8_t* q, uint8_t* scale_t, void* stream);
 
 /* Thread-local message describing the calling thread's last failure ("" if none). */
-GFG_API const char* gfg_last_error(void);
+GFG_API const char* grouped_fp8_last_error(void);
 
 /* Library version string. */
 GFG_API const char* gfg_version(void);

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = gfg.load_library()
     names = _declared_functions()
     assert {"grouped_fp8_gemm_contiguous", "grouped_fp8_gemm_masked", "fp8_quantize_act_1x128",
-            "fp8_quantize_weight_128x128", "gfg_last_error", "gfg_version"} <= set(names)
+            "fp8_quantize_weight_128x128", "grouped_fp8_last_error", "gfg_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -125,9 +125,9 @@ def test_device_quantizer_argument_errors():
     assert q(0x1000, 0, 1, 4, (1 << 24) + 128, 0x1000, 0x1000) == 2   # K above 2^24
     assert q(0x1000, 0, 1, (1 << 30) + 1, 128, 0x1000, 0x1000) == 2   # M above 2^30
     assert q(0x1000, 0, 65535, 1 << 20, 1 << 14, 0x1000, 0x1000) == 2  # 2^31 or more triples
-    assert "2^31" in gfg.load_library().gfg_last_error().decode()
+    assert "2^31" in gfg.load_library().grouped_fp8_last_error().decode()
     assert q(0x1008, 0, 1, 4, 128, 0x1000, 0x1000) == 1          # x not 16-byte aligned
-    assert "16-byte" in gfg.load_library().gfg_last_error().decode()
+    assert "16-byte" in gfg.load_library().grouped_fp8_last_error().decode()
 
 
 # Host-side argument checks of the GEMM entry points: these return before any
@@ -160,7 +160,7 @@ def test_gemm_argument_errors(fn):
     assert fn(K=-128) == 1
     assert fn(N=200) == 2          # ragged N: outside the kernels' tiling
     assert fn(K=300) == 2
-    msg = gfg.load_library().gfg_last_error().decode()
+    msg = gfg.load_library().grouped_fp8_last_error().decode()
     assert "multiples of 128" in msg
 
 
@@ -171,6 +171,26 @@ def test_gemm_empty_and_oversize():
     assert _m(Mmax=-5) == 1
     assert _c(M=4096 * 128 + 1) == 2
     assert _m(G=33, Mmax=128 * 128) == 2
+
+
+def test_32bit_extent_bounds():
+    """One expert's B (N*K bytes) and the A-scale tensor are addressed with
+    32-bit offsets in the kernels; larger extents are refused before any launch
+    (including the up rows of silu_mul, which lie N/2 rows past the gate rows).
+    The accepted edge cases use zero rows, so nothing is launched."""
+    assert _c(N=1 << 20, K=1 << 12) == 2                      # N*K = 2^32
+    assert "2^32" in gfg.load_library().grouped_fp8_last_error().decode()
+    assert _c(N=1 << 19, K=1 << 12, M=0) == 0                 # 2^31: accepted
+    assert _sc(I=1 << 19, K=1 << 13) == 2                     # 2I*K = 2^33
+    assert _sm(I=1 << 19, K=1 << 13) == 2
+    assert _sc(I=1 << 17, K=1 << 13, M=0) == 0                # 2^31: accepted
+    # A-scale tensor [K/128][M]: 2^19 rows x 2^16 blocks = 2^35 bytes
+    assert _c(M=1 << 19, N=128, K=1 << 23) == 2
+    assert "A-scale" in gfg.load_library().grouped_fp8_last_error().decode()
+    assert _m(G=1, Mmax=1 << 19, N=128, K=1 << 23) == 2
+    # MXFP8: one scale byte per 32 K elements: 2^19 rows x 2^13 = 2^32
+    assert gfg.raw_mx_contiguous(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 19, 256, 1 << 18, 1, 0, 0) == 2
+    assert gfg.raw_mx_contiguous(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, 1 << 18, 1, 0, 0) == 0
 
 
 def _sc(**kw):
@@ -197,11 +217,11 @@ def test_silu_mul_argument_errors(fn):
     assert fn(I=-128) == 1
     assert fn(K=300) == 2
     assert fn(I=192) == 2          # I must be a multiple of 128 (the output tile)
-    assert "multiple of 128" in gfg.load_library().gfg_last_error().decode()
+    assert "multiple of 128" in gfg.load_library().grouped_fp8_last_error().decode()
     assert fn(sa=FAKE + 2) == 2    # the packed A-scale words need 4-byte alignment
     rows = {"M": 258} if fn is _sc else {"Mmax": 258}
     assert fn(**rows) == 2         # scale rows not a multiple of 4
-    assert "multiple of 4" in gfg.load_library().gfg_last_error().decode()
+    assert "multiple of 4" in gfg.load_library().grouped_fp8_last_error().decode()
 
 
 def test_silu_mul_empty_is_noop():
@@ -284,7 +304,7 @@ def test_mx_gemm_argument_errors(fn):
     assert fn(G=0) == 1
     assert fn(K=300) == 2
     assert fn(N=384) == 2          # N must be a multiple of 256
-    assert "multiple of 256" in gfg.load_library().gfg_last_error().decode()
+    assert "multiple of 256" in gfg.load_library().grouped_fp8_last_error().decode()
     assert fn(sa=FAKE + 1) == 2
     assert fn(sb=FAKE + 2) == 2
     rows = {"M": 130} if fn is _mc else {"Mmax": 130}
@@ -355,7 +375,7 @@ def test_mx4_gemm_argument_errors(contig):
         assert call(**{k: None}) == 1, k
     assert call(K=0) == 1
     assert call(K=384) == 2            # K (elements) must be a multiple of 256
-    assert "multiple of 256" in gfg.load_library().gfg_last_error().decode()
+    assert "multiple of 256" in gfg.load_library().grouped_fp8_last_error().decode()
     assert call(N=384) == 2
     assert call(M=130) == 2
     assert call(sb=FAKE + 2) == 2
@@ -380,9 +400,9 @@ def test_mx4_silu_mul_argument_errors(contig):
     assert call(K=0) == 1
     assert call(I=0) == 1
     assert call(K=384) == 2            # K (E2M1 elements) must be a multiple of 256
-    assert "multiple of 256" in gfg.load_library().gfg_last_error().decode()
+    assert "multiple of 256" in gfg.load_library().grouped_fp8_last_error().decode()
     assert call(I=192) == 2            # I must be a multiple of 128 (the output tile)
-    assert "multiple of 128" in gfg.load_library().gfg_last_error().decode()
+    assert "multiple of 128" in gfg.load_library().grouped_fp8_last_error().decode()
     assert call(M=130) == 2            # scale rows not a multiple of 4
     assert call(sa=FAKE + 2) == 2
     assert call(sb=FAKE + 2) == 2
