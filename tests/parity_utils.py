@@ -13,11 +13,14 @@ SENTINEL = -12352.0          # exactly representable in bf16 and f16
 CALC_DIFF_MAX = 1e-5         # GPU vs fp64 oracle
 MAX_REL_MAX = 1e-2           # row-floored max relative error
 # Denominator floor of the relative error, as a fraction of the row's largest
-# |output|.  gfx950's scaled FP8 MFMA sums each 128-product block with reduced
-# internal precision (one block: ~1.4e-3 relative; K=7168: ~5e-5 of the output
-# rms, against ~7e-7 for exact fp32 sums), so outputs that cancel to near zero
-# carry an absolute error set by the row's scale, not their own; 1% of the row
-# maximum is where that error stays far below the 1e-2 bound.
+# |output|.  gfx950's scaled FP8 MFMA does not sum a 128-wide K block in fp32:
+# inside a 16-element K group it drops products 2^-14 below the group's
+# largest, and on N(0,1) data one block's error reaches ~2e-4 of the sum of
+# |products| (measured through the C-ABI in tests/test_gpu_mfma_precision.py).
+# Outputs that cancel to near zero therefore carry an absolute error set by
+# the row's scale, not their own: at a floor of 1e-3 of the row maximum a
+# single K block already exceeds 1e-2; at 1e-2 of the row maximum the bound
+# holds.  check_close reports both.
 REL_FLOOR = 1e-2
 
 

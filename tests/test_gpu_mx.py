@@ -94,48 +94,3 @@ def test_mx_exact_integer_case_bitwise(out):
     rnd = o.round_to_bf16 if out == "bf16" else o.round_to_f16
     want = torch.from_numpy(rnd(exact)).to(torch_dtype(out))
     assert np.array_equal(bits(d), bits(want))
-
-
-def _mx_sampled(w, qa, sa, d_bits_out, got_all, x, rng):
-    """Oracle on sampled rows of each of up to 12 experts, every column."""
-    layout = x["grouped_layout"]
-    experts = sorted(set([0, w.G - 1] + [int(v) for v in rng.choice(w.G, size=min(10, w.G), replace=False)]))
-    bq, bs = {}, {}
-    gots, refs = [], []
-    for g in experts:
-        rows = np.nonzero(layout == g)[0]
-        if not rows.size:
-            continue
-        pick = sorted(set([rows[0], rows[-1]] + [int(v) for v in rng.choice(rows, size=min(2, rows.size), replace=False)]))
-        k = int(x["b_index"][g]) if "b_index" in x else g
-        if k not in bq:
-            bq[k], bs[k] = o.quantize_mx_1x32(x["b"][k:k + 1])
-        oqa, osa = o.quantize_mx_1x32(x["a"][pick])
-        assert np.array_equal(qa[pick], oqa) and np.array_equal(sa[:, pick], osa)
-        refs.append(o.grouped_gemm_mx_contiguous(oqa, osa, bq[k], bs[k], np.zeros(len(pick), np.int32)))
-        gots.append(got_all[pick])
-    check_close(np.concatenate(gots), np.concatenate(refs), w.name)
-
-
-@pytest.mark.parametrize("name", ["mx_contig_g4_m1024_n2048_k7168", "mx_kimi_tp4_gemm1_t4096"])
-def test_mx_workload_full_size(name):
-    """Full-size MX workloads in the benchmark's launch configuration; the oracle
-    recomputes sampled rows of up to 12 experts across every column."""
-    w = wl.workload(name)
-    print(f"[mx] {w.name} M={w.M} N={w.N} K={w.K} G={w.G}", flush=True)
-    x = wl.draw(w)
-    layout = x["grouped_layout"]
-    qa, sa = gfg.fp8_quantize_mx_1x32(x["a"])
-    qb, sb = gfg.fp8_quantize_mx_1x32(x["b"])
-    qb_d, sb_d = to_dev(qb), to_dev(sb)
-    if w.b_distinct:
-        idx = torch.from_numpy(x["b_index"]).cuda()
-        qb_d, sb_d = qb_d.index_select(0, idx), sb_d.index_select(0, idx)
-    d = torch.full((w.M, w.N), SENTINEL, dtype=torch_dtype(w.out_dtype), device="cuda")
-    gfg.grouped_mxfp8_gemm_contiguous(to_dev(qa), to_dev(sa), qb_d, sb_d, to_dev(layout), d)
-    torch.cuda.synchronize()
-    del qb_d, sb_d
-    assert np.all(bits(d)[layout < 0] == sentinel_bits(w.out_dtype)), "padding rows were written"
-    got_all = d.float().cpu().numpy()
-    del d
-    _mx_sampled(w, qa, sa, None, got_all, x, np.random.default_rng(w.seed))

@@ -92,39 +92,3 @@ def test_mx4_exact_integer_case_bitwise(out):
     rnd = o.round_to_bf16 if out == "bf16" else o.round_to_f16
     want = torch.from_numpy(rnd(exact)).to(torch_dtype(out))
     assert np.array_equal(bits(d), bits(want))
-
-
-@pytest.mark.parametrize("name", ["mx4_contig_g4_m1024_n2048_k7168", "mx4_kimi_tp4_gemm1_t4096"])
-def test_mx4_workload_full_size(name):
-    w = wl.workload(name)
-    print(f"[mx4] {w.name} M={w.M} N={w.N} K={w.K} G={w.G}", flush=True)
-    x = wl.draw(w)
-    layout = x["grouped_layout"]
-    qa, sa = gfg.fp4_quantize_mx_1x32(x["a"])
-    qb, sb = gfg.fp4_quantize_mx_1x32(x["b"])
-    qb_d, sb_d = to_dev(qb), to_dev(sb)
-    if w.b_distinct:
-        idx = torch.from_numpy(x["b_index"]).cuda()
-        qb_d, sb_d = qb_d.index_select(0, idx), sb_d.index_select(0, idx)
-    d = torch.full((w.M, w.N), SENTINEL, dtype=torch_dtype(w.out_dtype), device="cuda")
-    gfg.grouped_mxfp4_gemm_contiguous(to_dev(qa), to_dev(sa), qb_d, sb_d, to_dev(layout), d)
-    torch.cuda.synchronize()
-    del qb_d, sb_d
-    assert np.all(bits(d)[layout < 0] == sentinel_bits(w.out_dtype)), "padding rows were written"
-    got_all = d.float().cpu().numpy()
-    del d
-    rng = np.random.default_rng(w.seed)
-    experts = sorted(set([0, w.G - 1] + [int(v) for v in rng.choice(w.G, size=min(10, w.G), replace=False)]))
-    bq = {}
-    gots, refs = [], []
-    for g in experts:
-        rows = np.nonzero(layout == g)[0]
-        pick = sorted(set([rows[0], rows[-1]] + [int(v) for v in rng.choice(rows, size=min(2, rows.size), replace=False)]))
-        k = int(x["b_index"][g]) if "b_index" in x else g
-        if k not in bq:
-            bq[k] = o.quantize_mx4_1x32(x["b"][k:k + 1])
-        oqa, osa = o.quantize_mx4_1x32(x["a"][pick])
-        assert np.array_equal(qa[pick], oqa) and np.array_equal(sa[:, pick], osa)
-        refs.append(o.grouped_gemm_mx4_contiguous(oqa, osa, *bq[k], np.zeros(len(pick), np.int32)))
-        gots.append(got_all[pick])
-    check_close(np.concatenate(gots), np.concatenate(refs), w.name)
