@@ -328,6 +328,10 @@ def main():
                     help="gemm: the grouped GEMM (the default); quant: the device activation quantizer "
                          "on the workload's A operand")
     ap.add_argument("--in-dtype", choices=("bf16", "f32"), default="bf16", help="--op quant input dtype")
+    ap.add_argument("--tile", choices=("auto", "128x256", "256x256"), default="auto",
+                    help="output tile of the plain FP8 GEMM (auto: chosen per launch)")
+    ap.add_argument("--num-xcd", type=int, default=8, help="XCDs the tile order is split over (1 or 8)")
+    ap.add_argument("--group-m", type=int, default=0, help="grouped-M width in M tiles (0: kernel default)")
     args = ap.parse_args()
     if args.op == "quant":
         if args.gpus != 1:
@@ -355,6 +359,8 @@ def main():
     from fp8_block_scaled_amd import workloads as wl
 
     gfg.load_library()
+    gfg.set_tile_shape({"auto": gfg.TILE_AUTO, "128x256": gfg.TILE_128x256, "256x256": gfg.TILE_256x256}[args.tile])
+    gfg.set_tile_order(args.num_xcd, args.group_m)
     w = wl.workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -457,7 +463,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "op": w.op, "layout": w.layout, "G": w.G, "N": w.N, "K": w.K,
                    "M_rows": w.M, "M_valid": w.m_valid, "out": w.out_dtype,
-                   "input_sets": nsets, "parallelism": "none (1 GPU)"},
+                   "input_sets": nsets, "parallelism": "none (1 GPU)", "tile": args.tile,
+                   "num_xcd": args.num_xcd, "group_m": args.group_m},
         "pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2),
         "pct_of_mfma_peak_for_dtype": round(100.0 * tflops / peak, 2),
         "roofline": roofline,

@@ -34,6 +34,7 @@ __all__ = [
     "grouped_mxfp4_gemm_contiguous", "grouped_mxfp4_gemm_masked", "fp4_quantize_mx_1x32",
     "raw_mx4_contiguous", "raw_mx4_masked",
     "OUT_BF16", "OUT_F16", "IN_F32", "IN_BF16",
+    "set_tile_order", "set_tile_shape", "set_grid_limit", "TILE_AUTO", "TILE_128x256", "TILE_256x256",
 ]
 
 # GFG_LIBRARY names another build of the library to load (the host-sanitizer
@@ -93,6 +94,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fp8_quantize_act_1x128_device.restype = ctypes.c_int
     lib.grouped_fp8_last_error.argtypes = []
     lib.grouped_fp8_last_error.restype = ctypes.c_char_p
+    lib.grouped_fp8_set_tile_order.argtypes = [i32, i32]
+    lib.grouped_fp8_set_tile_order.restype = ctypes.c_int
+    lib.grouped_fp8_set_tile_shape.argtypes = [i32]
+    lib.grouped_fp8_set_tile_shape.restype = ctypes.c_int
+    lib.grouped_fp8_set_grid_limit.argtypes = [i32]
+    lib.grouped_fp8_set_grid_limit.restype = ctypes.c_int
     lib.gfg_version.argtypes = []
     lib.gfg_version.restype = ctypes.c_char_p
     if path is None:
@@ -103,6 +110,25 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 def _check(rc: int):
     if rc != 0:
         raise GfgError(rc, load_library().grouped_fp8_last_error().decode())
+
+
+# ------------------------------------------------------------------ launch settings
+TILE_AUTO, TILE_128x256, TILE_256x256 = 0, 1, 2
+
+
+def set_tile_order(num_xcd: int = 8, group_m: int = 0) -> None:
+    """XCD split and grouped-M width of the tile order (process-wide)."""
+    _check(load_library().grouped_fp8_set_tile_order(num_xcd, group_m))
+
+
+def set_tile_shape(shape: int = TILE_AUTO) -> None:
+    """Output tile of the plain FP8 GEMM calls: TILE_AUTO, TILE_128x256 or TILE_256x256."""
+    _check(load_library().grouped_fp8_set_tile_shape(shape))
+
+
+def set_grid_limit(max_workgroups: int = 0) -> None:
+    """Cap the workgroups of a GEMM launch (0: one per CU)."""
+    _check(load_library().grouped_fp8_set_grid_limit(max_workgroups))
 
 
 # ------------------------------------------------------------------ raw pointer calls

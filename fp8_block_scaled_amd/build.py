@@ -38,13 +38,15 @@ def build(verbose: bool = False) -> str:
     steps = [
         [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "gfg_gemm.hip"),
          "-o", os.path.join(out_dir, "gfg_gemm.o")],
+        [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "gfg_gemm256.hip"),
+         "-o", os.path.join(out_dir, "gfg_gemm256.o")],
         [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "gfg_quant.hip"),
          "-o", os.path.join(out_dir, "gfg_quant.o")],
         ["g++", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-pthread", "-I", INCLUDE, "-I", CSRC, "-c",
          os.path.join(CSRC, "gfg_host.cpp"), "-o", os.path.join(out_dir, "gfg_host.o")],
     ]
-    objs = [os.path.join(out_dir, "gfg_gemm.o"), os.path.join(out_dir, "gfg_quant.o"),
-            os.path.join(out_dir, "gfg_host.o")]
+    objs = [os.path.join(out_dir, "gfg_gemm.o"), os.path.join(out_dir, "gfg_gemm256.o"),
+            os.path.join(out_dir, "gfg_quant.o"), os.path.join(out_dir, "gfg_host.o")]
     tmp = LIB + ".tmp"
     steps.append([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp])
     for cmd in steps:
@@ -87,11 +89,13 @@ def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:
         [hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-c", os.path.join(CSRC, "gfg_gemm.hip"), "-o", o("gfg_gemm.o")],
         [hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops", "-c", os.path.join(CSRC, "gfg_gemm256.hip"), "-o", o("gfg_gemm256.o")],
+        [hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-c", os.path.join(CSRC, "gfg_quant.hip"), "-o", o("gfg_quant.o")],
         [clang, *common, "-pthread", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-c",
          os.path.join(CSRC, "gfg_host.cpp"), "-o", o("gfg_host.o")],
         [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *SAN_HOST[:4], "-shared-libasan",
-         o("gfg_gemm.o"), o("gfg_quant.o"), o("gfg_host.o"), "-o", o("libgfg_san.so")],
+         o("gfg_gemm.o"), o("gfg_gemm256.o"), o("gfg_quant.o"), o("gfg_host.o"), "-o", o("libgfg_san.so")],
     ]
     for cmd in steps:
         if verbose:

@@ -27,9 +27,11 @@
 //  * the MFMA's first operand is the B tile (N rows) and its second the A
 //    tile (M rows), so a lane's accumulators hold output columns of one row;
 //    on the 256-column tile, B fragment x takes the wave's columns 4*l16 + x,
-//    which hands each lane 16 consecutive columns of its row, written as two
-//    16-byte stores (4 consecutive columns and one 8-byte store per fragment
-//    on the 128-column tile and for silu_mul).
+//    which hands each lane 16 consecutive columns of its row; one DPP swap
+//    between neighbouring lanes then makes every 16-byte store instruction
+//    write eight whole 128-byte lines, sent non-temporal (4 consecutive
+//    columns and one 8-byte store per fragment on the 128-column tile and for
+//    silu_mul).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -37,6 +39,7 @@
 #include <vector>
 
 #include "gfg.h"
+#include "gfg_device.h"
 #include "gfg_internal.h"
 
 namespace gfg {
@@ -46,26 +49,6 @@ constexpr int BM = 128;          // rows of A per tile (= scale block edge)
 constexpr int BK = 128;          // K per step (= one E8M0 block along K)
 constexpr int NTHREADS = 512;    // 8 wave64s, two per SIMD
 constexpr int MT_MAX = 4096;     // largest number of candidate 128-row tiles
-constexpr int NUM_XCD = 8;
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-struct Params {
-    const uint8_t* a;        // contiguous [M][K]; masked [G][Mmax][K]
-    const uint8_t* a_scale;  // contiguous [KB][M]; masked [G][KB][Mmax]
-    const uint8_t* b;        // [G][N][K]
-    const uint8_t* b_scale;  // [G][NB][KB]
-    const int32_t* meta;     // grouped_layout [M] or masked_m [G]
-    void* d;                 // contiguous [M][N]; masked [G][Mmax][N]
-    int64_t rows;            // contiguous: M; masked: Mmax
-    int N, K, G;
-    int n_cand;              // candidate 128-row tiles: ceil(M/128) or G*ceil(Mmax/128)
-    int mt_per_group;        // masked: ceil(Mmax/128)
-    int group_m;             // grouped-M width (in 128-row tiles) when the tiles take more than two rounds
-};
-
 // Byte offset of 16-byte chunk c (0..7) of row r inside a [rows][128 B] LDS tile.
 // XORing the chunk with r & 7 makes both access patterns conflict-free on
 // gfx950 (measured with SQ_LDS_BANK_CONFLICT): the MFMA fragment read (16
@@ -99,40 +82,6 @@ __device__ __forceinline__ bool cand_valid(const Params& p, int c, int* aux) {
         *aux = g;
         return g >= 0 && g < p.G;
     }
-}
-
-#define GFG_LDS __attribute__((address_space(3)))
-
-// s_waitcnt immediate (gfx9 encoding): wait until at most VM vector-memory
-// loads and LG LDS/scalar operations of this wave are outstanding.
-#define GFG_WAITCNT(VM, LG) \
-    __builtin_amdgcn_s_waitcnt(((VM) & 15) | ((((VM) >> 4) & 3) << 14) | (7 << 4) | (((LG) & 15) << 8))
-
-// Raw buffer resource over [base, base + bytes): stride 0, 32-bit data format.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
-}
-
-// A wave-uniform pointer re-materialized from scalar registers.
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
-    return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
-}
-
-// The 4-byte word holding scale byte kb of a wave's scale_b row, read through
-// the scalar data cache into a scalar register (the byte is extracted where it
-// is used).  A scalar load is counted by lgkmcnt, which every K-step drains
-// anyway, so it never makes the compiler wait on the vector-memory counter
-// (and with it on the LDS DMA in flight).  An aligned word that contains a
-// byte of an allocation lies in the same page as that byte.
-typedef const __attribute__((address_space(4))) uint32_t sword_t;
-__device__ __forceinline__ int load_scale_word(const uint8_t* row, int kb) {
-    return int(*reinterpret_cast<sword_t*>(reinterpret_cast<uintptr_t>(row + kb) & ~uintptr_t(3)));
-}
-__device__ __forceinline__ int scale_byte(int word, const uint8_t* row, int kb) {
-    return (word >> (8 * int((reinterpret_cast<uintptr_t>(row) + uintptr_t(kb)) & 3))) & 0xff;
 }
 
 // Per-tile, per-lane constants of the K loop.  SAW: the lane's four A-scale
@@ -488,11 +437,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
     const unsigned T = unsigned(n_mtiles) * unsigned(NT);
 
     // ---- 2. this workgroup's share: a contiguous range per XCD -------------
-    const unsigned xcd = blockIdx.x % NUM_XCD, slot = blockIdx.x / NUM_XCD;
-    const unsigned slots = gridDim.x / NUM_XCD;
-    const unsigned per = T / NUM_XCD, rem = T % NUM_XCD;
-    const unsigned x_start = xcd * per + (xcd < rem ? xcd : rem);
-    const unsigned x_count = per + (xcd < rem ? 1u : 0u);
+    TileOrder order;
+    order.init(T, p.num_xcd);
 
     const int KB = p.K / BK;
     const int NB = p.N / 128;
@@ -504,21 +450,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
     GFG_LDS uint8_t* const buf1 = (GFG_LDS uint8_t*)smem1;
     GFG_LDS uint8_t* const buf2 = (GFG_LDS uint8_t*)smem2;
 
-    for (unsigned i = slot; i < x_count; i += slots) {
+    for (unsigned i = order.slot; i < order.x_count; i += order.slots) {
         // grouped-M order over (valid m-tile rank, n-tile).  When every
         // workgroup has at most two tiles, an XCD's 32 concurrent tiles span
         // 8 m-tiles x 4 n-tiles: on the 128 x 256 tile that streams 8*128 +
         // 4*256 rows of K bytes into its L2 per round instead of 4*128 + 8*256
         // (4 x 8), a fifth less.  Longer walks keep the narrower group_m.
-        const unsigned t = x_start + i;
-        const unsigned gm = T <= 2u * gridDim.x ? 8u : unsigned(p.group_m);
-        const unsigned per_group = gm * unsigned(NT);
-        const unsigned grp = t / per_group;
-        const unsigned first = grp * gm;
-        const unsigned gsz = min(gm, unsigned(n_mtiles) - first);   // shortened final group
-        const unsigned in_grp = t - grp * per_group;
-        const int r_rank = int(first + in_grp % gsz);
-        const int nt = int(in_grp / gsz);
+        // (A caller-chosen group_m overrides both.)
+        const unsigned gm = p.group_m > 0 ? unsigned(p.group_m) : (T <= 2u * gridDim.x ? 8u : 4u);
+        int r_rank, nt;
+        order.item(i, gm, unsigned(NT), unsigned(n_mtiles), &r_rank, &nt);
 
         const int cand = __builtin_amdgcn_readfirstlane(int(tile_list[r_rank]));
         const int aux = __builtin_amdgcn_readfirstlane(int(tile_aux[r_rank]));
@@ -722,6 +663,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             }
             continue;
         }
+        if constexpr (C::BL && !SILU) {
+            // Lane (l16, lq) holds 16-byte chunks 2lq + h (h = 0, 1) of the
+            // 128-byte line of row 4*l16 + y.  Swapping lane bit 0 with h (DPP
+            // quad_perm 1,0,3,2) hands slot h of the lane chunk 2lq + (l16 & 1)
+            // of row 4*((l16 & ~1) | h) + y, so each store instruction writes
+            // eight whole lines; those go out non-temporal.  The validity bits
+            // of the rows a slot now holds come from the quad lane that owned them.
+            typedef OutT out8 __attribute__((ext_vector_type(8)));
+            typedef float f8v __attribute__((ext_vector_type(8)));
+            int okm = 0;
+#pragma unroll
+            for (int y = 0; y < FM; ++y) {
+                const int row = int(m0) + wm * 64 + 4 * l16 + y;
+                okm |= int(row < mlimit && (MASKED || int(lay[y]) == g)) << y;
+            }
+            const int okh[2] = {__builtin_amdgcn_update_dpp(0, okm, 0xA0, 0xF, 0xF, false),
+                                __builtin_amdgcn_update_dpp(0, okm, 0xF5, 0xF, 0xF, false)};
+            const bool odd = (lane & 1) != 0;
+            OutT* const dcol = reinterpret_cast<OutT*>(d_reg) + n0 + wn * WN + 16 * lq + 8 * (lane & 1);
+#pragma unroll
+            for (int y = 0; y < FM; ++y) {
+                u32x4 P[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const v4f c0 = acc[0][y], c1 = acc[1][y], c2 = acc[2][y], c3 = acc[3][y];
+                    const f8v v = {c0[2 * h], c1[2 * h], c2[2 * h], c3[2 * h],
+                                   c0[2 * h + 1], c1[2 * h + 1], c2[2 * h + 1], c3[2 * h + 1]};
+                    P[h] = __builtin_bit_cast(u32x4, __builtin_convertvector(v, out8));
+                }
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t a = P[0][d], b = P[1][d];
+                    const uint32_t ax = uint32_t(__builtin_amdgcn_update_dpp(0, int(a), 0xB1, 0xF, 0xF, false));
+                    const uint32_t bx = uint32_t(__builtin_amdgcn_update_dpp(0, int(b), 0xB1, 0xF, 0xF, false));
+                    P[0][d] = odd ? bx : a;
+                    P[1][d] = odd ? b : ax;
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (!((okh[h] >> y) & 1)) continue;
+                    const int row = int(m0) + wm * 64 + 4 * ((l16 & ~1) | h) + y;
+                    __builtin_nontemporal_store(P[h], reinterpret_cast<u32x4*>(dcol + int64_t(row) * p.N));
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int y = 0; y < FM; ++y) {
             const int row = int(m0) + wm * 64 + 4 * l16 + y;   // rows of a region fit in 32 bits
@@ -779,6 +766,17 @@ int device_info(DeviceInfo* out) {
     return GFG_OK;
 }
 
+}  // namespace
+
+int device_cus(int* cus) {
+    DeviceInfo di;
+    if (int rc = device_info(&di)) return rc;
+    *cus = di.cus;
+    return GFG_OK;
+}
+
+namespace {
+
 template <int BN, bool MASKED, bool SAW, typename OutT, bool SILU = false, bool MX = false, bool MX4 = false>
 int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     DeviceInfo di;
@@ -786,7 +784,10 @@ int launch_t(const Params& p, unsigned n_cand_tiles, hipStream_t s) {
     const unsigned NT = unsigned(p.N / BN);
     const unsigned upper = n_cand_tiles * NT;                 // valid tiles cannot exceed this
     unsigned grid = upper < unsigned(di.cus) ? upper : unsigned(di.cus);
-    grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;          // whole slots on every XCD
+    const int lim = grid_limit();
+    if (lim > 0 && grid > unsigned(lim)) grid = unsigned(lim);
+    const unsigned nx = unsigned(p.num_xcd);
+    grid = (grid + nx - 1) / nx * nx;                         // whole slots on every XCD
     if (grid == 0) return GFG_OK;
     hipLaunchKernelGGL((grouped_fp8_gemm_kernel<BN, MASKED, SAW, OutT, SILU, MX, MX4>), dim3(grid), dim3(NTHREADS), 0,
                        s, p);
@@ -810,9 +811,45 @@ int dispatch_w(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
 
 // The packed A-scale path needs every scale row (and so every aligned group of
 // four rows) to start on a 4-byte boundary.
+//
+// Tile shape: the 256 x 256 kernel (gfg_gemm256.hip) moves a third fewer bytes
+// per FLOP through the global -> LDS path than the 128 x 256 one, but has half
+// as many tiles; it is chosen when it still gives every CU at least one tile
+// (counted from the candidate M tiles, an upper bound for the masked layout)
+// and its requirements hold: N a multiple of 256 and at most 2^22, K / 128
+// even, packed A-scale words.
 template <bool MASKED>
 int dispatch(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
     const bool saw = p.rows % 4 == 0 && reinterpret_cast<uintptr_t>(p.a_scale) % 4 == 0;
+    const int choice = tile_shape_choice();
+    const bool fits256 = saw && p.N % 256 == 0 && p.N <= (1 << 22) && (p.K / 128) % 2 == 0;
+    if (choice == GFG_TILE_256x256 && !fits256)
+        return fail(GFG_EUNSUPPORTED,
+                    "256 x 256 tiles need N a multiple of 256 (<= 2^22), K/128 even, scale rows a multiple of 4 "
+                    "and scale_a 4-byte aligned");
+    if (fits256 && choice != GFG_TILE_128x256) {
+        Params q = p;
+        unsigned nc = n_cand;
+        if (MASKED) {
+            q.mt_per_group = int((p.rows + 255) / 256);
+            q.n_cand = q.mt_per_group * p.G;
+            nc = unsigned(q.n_cand);
+        }
+        // Automatic choice (from timings of both shapes): the 256 x 256 tile
+        // pays a larger fixed cost per launch (its first stages and last
+        // output stores are not overlapped with MFMAs) and a quarter of its
+        // tile is idle on the half tiles at run ends, so it wins when every CU
+        // walks at least four of its tiles, or one of them with a long K loop
+        // (64 steps or more).  Masked launches count from the host-side upper
+        // bound (masked_m lives in device memory), so only the first rule
+        // applies to them.
+        const uint64_t tiles = uint64_t(MASKED ? nc : (n_cand + 1) / 2) * unsigned(p.N / 256);
+        int cus = 0;
+        if (int rc = device_cus(&cus)) return rc;
+        const bool many = tiles >= 4 * uint64_t(cus);
+        const bool long_k = !MASKED && tiles >= uint64_t(cus) && p.K / BK >= 64;
+        if (choice == GFG_TILE_256x256 || many || long_k) return launch_gemm256(q, MASKED, nc, out_dtype, s);
+    }
     return saw ? dispatch_w<MASKED, true>(p, n_cand, out_dtype, s) : dispatch_w<MASKED, false>(p, n_cand, out_dtype, s);
 }
 
@@ -848,8 +885,6 @@ int check_scale_extent(const char* fn, int64_t rows, int64_t K, int sk) {
     return GFG_OK;
 }
 
-int group_m_default() { return 4; }
-
 // Parameters of a contiguous call: M rows of A mapped to experts by
 // grouped_layout, B [G][N][K].  Returns GFG_OK with *n_cand set, or an error.
 int contig_params(const char* fn, const void* a, const uint8_t* a_scale, const void* b, const uint8_t* b_scale,
@@ -874,7 +909,8 @@ int contig_params(const char* fn, const void* a, const uint8_t* a_scale, const v
     p->G = G;
     p->n_cand = int(*n_cand);
     p->mt_per_group = 0;
-    p->group_m = group_m_default();
+    p->group_m = locality_group_m();
+    p->num_xcd = locality_num_xcd();
     return GFG_OK;
 }
 
@@ -902,7 +938,8 @@ int masked_params(const char* fn, const void* a, const uint8_t* a_scale, const v
     p->G = G;
     p->n_cand = int(*n_cand);
     p->mt_per_group = int(per);
-    p->group_m = group_m_default();
+    p->group_m = locality_group_m();
+    p->num_xcd = locality_num_xcd();
     return GFG_OK;
 }
 

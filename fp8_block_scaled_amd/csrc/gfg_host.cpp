@@ -8,6 +8,7 @@
 // activations, stored transposed [ceil(K/128)][M]; (128,128) blocks for
 // weights.  E4M3 values are rounded to nearest, ties to even.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -34,6 +35,15 @@ int fail(int code, const char* fmt, ...) {
 }
 
 void clear_error() { t_last_error.clear(); }
+
+static std::atomic<int> g_num_xcd{8};
+static std::atomic<int> g_group_m{0};
+static std::atomic<int> g_tile_shape{0};
+static std::atomic<int> g_grid_limit{0};
+int locality_num_xcd() { return g_num_xcd.load(std::memory_order_relaxed); }
+int locality_group_m() { return g_group_m.load(std::memory_order_relaxed); }
+int tile_shape_choice() { return g_tile_shape.load(std::memory_order_relaxed); }
+int grid_limit() { return g_grid_limit.load(std::memory_order_relaxed); }
 
 namespace {
 
@@ -149,7 +159,34 @@ using namespace gfg;
 
 extern "C" const char* grouped_fp8_last_error(void) { return t_last_error.c_str(); }
 
-extern "C" const char* gfg_version(void) { return "gfg 0.1 gfx950"; }
+extern "C" const char* gfg_version(void) { return "gfg 0.2 gfx950"; }
+
+extern "C" int grouped_fp8_set_tile_order(int32_t num_xcd, int32_t group_m) {
+    clear_error();
+    if (num_xcd < 1 || num_xcd > 8)
+        return fail(GFG_EINVAL, "grouped_fp8_set_tile_order: num_xcd=%d outside [1, 8]", num_xcd);
+    if (group_m < 0 || group_m > 64)
+        return fail(GFG_EINVAL, "grouped_fp8_set_tile_order: group_m=%d outside [0, 64]", group_m);
+    g_num_xcd.store(num_xcd, std::memory_order_relaxed);
+    g_group_m.store(group_m, std::memory_order_relaxed);
+    return GFG_OK;
+}
+
+extern "C" int grouped_fp8_set_grid_limit(int32_t max_workgroups) {
+    clear_error();
+    if (max_workgroups < 0)
+        return fail(GFG_EINVAL, "grouped_fp8_set_grid_limit: max_workgroups=%d is negative", max_workgroups);
+    g_grid_limit.store(max_workgroups, std::memory_order_relaxed);
+    return GFG_OK;
+}
+
+extern "C" int grouped_fp8_set_tile_shape(int32_t shape) {
+    clear_error();
+    if (shape < GFG_TILE_AUTO || shape > GFG_TILE_256x256)
+        return fail(GFG_EINVAL, "grouped_fp8_set_tile_shape: shape=%d is not a GFG_TILE_* value", shape);
+    g_tile_shape.store(shape, std::memory_order_relaxed);
+    return GFG_OK;
+}
 
 extern "C" int fp8_quantize_act_1x128(const float* x, int64_t M, int64_t K,
                                       uint8_t* q, uint8_t* scale_t) {

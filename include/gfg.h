@@ -300,6 +300,44 @@ GFG_API int fp8_quantize_weight_128x128(const float* w, int32_t G, int64_t N, in
 GFG_API int fp8_quantize_act_1x128_device(const void* x, int32_t in_dtype, int32_t G, int64_t M, int64_t K,
                                           uint8_t* q, uint8_t* scale_t, void* stream);
 
+/*
+ * Launch settings (process-wide, read at every GEMM call; not synchronized
+ * with calls in flight on other threads).
+ *
+ * grouped_fp8_set_tile_order: the order in which a launch walks its
+ * (M tile, N tile) work items.  The items are split into num_xcd contiguous
+ * ranges, one per XCD (the hardware deals workgroup w to XCD w % 8, so with
+ * num_xcd = 8 each range stays in one XCD's L2), and inside a range they
+ * follow a grouped-M order group_m M tiles wide.  This is the locality mapping
+ * of the second reference page ("[Kernel][MI350] Add cache-aware 8-wave
+ * BF16/FP16 GEMM", section "Changes": XCD remap and grouped-M traversal with
+ * a shortened final group, composed), made a run-time choice for its ablation
+ * (section "Performance", second table).  Defaults: num_xcd = 8, group_m = 0
+ * (each kernel's own width).  Every setting gives the same bytes: only the
+ * order of the tiles changes.  num_xcd in [1, 8], group_m in [0, 64], else
+ * GFG_EINVAL.
+ *
+ * grouped_fp8_set_tile_shape: the output tile of the plain FP8 GEMM calls
+ * (grouped_fp8_gemm_contiguous / _masked).  GFG_TILE_AUTO picks 256 x 256
+ * (where its requirements hold) when the launch has at least four such tiles
+ * per CU, or, for the contiguous layout, at least one per CU and K >= 8192;
+ * else 128 x 256.  (The masked layout counts from M_max: masked_m is device
+ * memory.)  GFG_TILE_256x256 needs N a multiple of 256 and
+ * at most 2^22, K/128 even, scale rows a multiple of 4 and scale_a 4-byte
+ * aligned; a call that misses them then returns GFG_EUNSUPPORTED.  Other
+ * values: GFG_EINVAL.  Results agree to the parity tolerance, not bit for
+ * bit: the two tiles sum each 128-K block's products in different groupings.
+ *
+ * grouped_fp8_set_grid_limit: at most max_workgroups workgroups per GEMM
+ * launch (0, the default: one per CU, fewer when there are fewer tiles).  The
+ * grid is then rounded up to a multiple of num_xcd.  Each workgroup walks
+ * more tiles; the results do not change.  Negative: GFG_EINVAL.
+ */
+enum gfg_tile_shape { GFG_TILE_AUTO = 0, GFG_TILE_128x256 = 1, GFG_TILE_256x256 = 2 };
+GFG_API int grouped_fp8_set_tile_order(int32_t num_xcd, int32_t group_m);
+GFG_API int grouped_fp8_set_tile_shape(int32_t shape);
+GFG_API int grouped_fp8_set_grid_limit(int32_t max_workgroups);
+
 /* Thread-local message describing the calling thread's last failure ("" if none). */
 GFG_API const char* grouped_fp8_last_error(void);
 

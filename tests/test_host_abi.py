@@ -408,3 +408,17 @@ def test_mx4_silu_mul_argument_errors(contig):
     assert call(sb=FAKE + 2) == 2
     assert call(M=0) == 0
     assert call(M=-4) == 1
+
+
+def test_launch_settings_argument_errors():
+    lib = gfg.load_library()
+    assert lib.grouped_fp8_set_tile_order(0, 0) == 1
+    assert lib.grouped_fp8_set_tile_order(9, 0) == 1
+    assert lib.grouped_fp8_set_tile_order(8, -1) == 1
+    assert lib.grouped_fp8_set_tile_order(8, 65) == 1
+    assert lib.grouped_fp8_set_tile_shape(3) == 1
+    assert lib.grouped_fp8_set_tile_shape(-1) == 1
+    assert lib.grouped_fp8_set_grid_limit(-1) == 1
+    assert lib.grouped_fp8_set_tile_order(1, 4) == 0 and lib.grouped_fp8_set_tile_order(8, 0) == 0
+    assert lib.grouped_fp8_set_tile_shape(2) == 0 and lib.grouped_fp8_set_tile_shape(0) == 0
+    assert lib.grouped_fp8_set_grid_limit(16) == 0 and lib.grouped_fp8_set_grid_limit(0) == 0
