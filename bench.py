@@ -34,19 +34,23 @@ PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA peak
 PEAK_FP4_TFLOPS = 10100.0         # MI355X dense FP4 (and FP6) MFMA peak
 PEAK_HBM_GBS = 8000.0
 RIDGE_FLOP_PER_BYTE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-DEFAULT_WORKLOAD = "contig_g4_m1024_n2048_k7168"
-KERNEL_SRC = os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", "gfg_gemm.hip")
-QUANT_SRC = os.path.join(ROOT, "fp8_block_scaled_amd", "csrc", "gfg_quant.hip")
+# The largest of the five reference workloads: 8 experts x 4096 rows, N=7168, K=2304.
+DEFAULT_WORKLOAD = "contig_g8_m4096_n7168_k2304_logmag"
+_CSRC = os.path.join(ROOT, "fp8_block_scaled_amd", "csrc")
+KERNEL_SRC = [os.path.join(_CSRC, n) for n in ("gfg_gemm.hip", "gfg_gemm256.hip", "gfg_device.h")]
+QUANT_SRC = [os.path.join(_CSRC, "gfg_quant.hip")]
 
 
-def kernel_source_hash(path=KERNEL_SRC) -> str:
-    """Hash of the kernel source's code: // comments and blank lines removed,
+def kernel_source_hash(paths=KERNEL_SRC) -> str:
+    """Hash of the kernel sources' code: // comments and blank lines removed,
     so an edit to comments alone keeps stored counter results valid."""
     import re
-    with open(path) as f:
-        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
-    code = "\n".join(ln for ln in lines if ln)
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    code = []
+    for path in paths:
+        with open(path) as f:
+            lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
+        code.append("\n".join(ln for ln in lines if ln))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def algorithmic_bytes(w, layout=None) -> int:
@@ -99,6 +103,34 @@ def _pmc_per_dispatch(root, counter):
                 if r["Counter_Name"] == counter:
                     per[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
     return {k: (sum(d.values()) / len(d), len(d)) for k, d in per.items()}
+
+
+def summarize_trace(root, last=100):
+    """Per-kernel durations from a rocprofv3 --kernel-trace csv run: calls,
+    mean over all dispatches, and the mean of the final `last` dispatches (the
+    timing protocol of the second reference page, section "Performance":
+    AMD_SERIALIZE_KERNEL=3 and the final 100 matching dispatches)."""
+    import collections
+    import csv
+    import glob
+    files = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {root}")
+    per = collections.defaultdict(list)
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+                per[r["Kernel_Name"]].append((t0, t1 - t0))
+    out = []
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        v.sort()
+        d = np.array([x for _, x in v], dtype=np.float64)
+        tail = d[-last:]
+        out.append({"kernel": name, "calls": len(d), "mean_ns": round(float(d.mean()), 1),
+                    f"final{last}_mean_ns": round(float(tail.mean()), 1), f"final{last}_min_ns": int(tail.min()),
+                    f"final{last}_max_ns": int(tail.max()), f"final{last}_std_ns": round(float(tail.std()), 1)})
+    return out
 
 
 def quant_traffic_path(w, in_dtype):
@@ -160,20 +192,46 @@ def _repeat_timed(fn):
             return dt / runs, runs
 
 
+CPU_SAMPLE_FLOPS = 2e12   # larger workloads time a bounded sample of one expert's rows
+
+
 def cpu_baseline(w, x):
     """The fp64 oracle (dequantize, then matmul) on the same workload, timed on
     the host.  Its own quantizer prepares the operands outside the timing; the
-    timed sample repeats until at least CPU_MIN_SECONDS of host time."""
+    timed sample repeats until at least CPU_MIN_SECONDS of host time.  `cores`
+    is the BLAS thread count the matmul ran with; `affinity_cores` the CPUs
+    the process may run on."""
     from threadpoolctl import threadpool_info
     from oracle import fp8_oracle as o
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    affinity = len(os.sched_getaffinity(0))
     quant_mx = o.quantize_mx4_1x32 if w.op in ("mx4", "mx4_silu") else o.quantize_mx_1x32
     gemm_mx = {"mx4": o.grouped_gemm_mx4_contiguous, "mx4_silu": o.grouped_gemm_mx4_silu_mul_contiguous}.get(
         w.op, o.grouped_gemm_mx_contiguous)
 
-    def result(flops, dt, runs, what):
-        return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-                "sample": f"{what}, {dt:.2f} s per run, {runs} runs; quantization untimed"}
+    def result(flops, dt, runs, what, parts=None):
+        r = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+             "affinity_cores": affinity, "kind": "oracle",
+             "sample": f"{what}, {dt:.2f} s per run, {runs} runs; quantization untimed"}
+        if parts:
+            r["parts_s"] = parts
+        return r
+
+    def parts_of(xa, xb, quant_a, gemm_fn):
+        """Seconds per run of the oracle's quantize (A and B), dequantize
+        (A and B) and grouped GEMM (which dequantizes, then multiplies), each
+        on the timed sample (one run each)."""
+        t0 = time.perf_counter()
+        qa, sa = quant_a(xa)
+        qb, sb = o.quantize_weight_128x128(xb)
+        t1 = time.perf_counter()
+        o.dequantize_act(qa.reshape(-1, qa.shape[-1]), sa.reshape(-1, sa.shape[-1]))
+        o.dequantize_weight(qb, sb)
+        t2 = time.perf_counter()
+        gemm_fn(qa, sa, qb, sb)
+        t3 = time.perf_counter()
+        return {"quantize": round(t1 - t0, 3), "dequantize": round(t2 - t1, 3),
+                "gemm_incl_dequantize": round(t3 - t2, 3)}
 
     if w.op in ("silu_mul", "mx4_silu") or (w.op in ("mx", "mx4") and w.b_distinct):
         # bounded sample: the rows of the first 16 experts (all 385 weight
@@ -204,11 +262,30 @@ def cpu_baseline(w, x):
         qa, sa = o.quantize_act_masked(x["a"])
         qb, sb = o.quantize_weight_128x128(x["b"])
         dt, runs = _repeat_timed(lambda: o.grouped_gemm_masked(qa, sa, qb, sb, w.masked_m))
-    else:
-        qa, sa = o.quantize_act_1x128(x["a"])
-        qb, sb = o.quantize_weight_128x128(x["b"])
-        dt, runs = _repeat_timed(lambda: o.grouped_gemm_contiguous(qa, sa, qb, sb, x["grouped_layout"]))
-    return result(w.flops, dt, runs, f"full steps of {w.name} (fp64 dequantize + matmul over all valid rows)")
+        parts = parts_of(x["a"], x["b"], o.quantize_act_masked,
+                         lambda qa, sa, qb, sb: o.grouped_gemm_masked(qa, sa, qb, sb, w.masked_m))
+        return result(w.flops, dt, runs, f"full steps of {w.name} (fp64 dequantize + matmul over all valid rows)",
+                      parts)
+    if w.flops > CPU_SAMPLE_FLOPS:
+        # bounded sample: the first rows of expert 0, against expert 0's weights
+        layout = x["grouped_layout"]
+        rows = np.nonzero(layout == 0)[0][:512]
+        xa, xb = x["a"][rows], x["b"][:1]
+        lay0 = np.zeros(rows.size, dtype=layout.dtype)
+        qa, sa = o.quantize_act_1x128(xa)
+        qb, sb = o.quantize_weight_128x128(xb)
+        dt, runs = _repeat_timed(lambda: o.grouped_gemm_contiguous(qa, sa, qb, sb, lay0))
+        parts = parts_of(xa, xb, o.quantize_act_1x128,
+                         lambda qa, sa, qb, sb: o.grouped_gemm_contiguous(qa, sa, qb, sb, lay0))
+        return result(2 * rows.size * w.N * w.K, dt, runs,
+                      f"the first {rows.size} rows of expert 0 of {w.name} against expert 0's {w.N}x{w.K} weights "
+                      f"(fp64 dequantize + matmul)", parts)
+    qa, sa = o.quantize_act_1x128(x["a"])
+    qb, sb = o.quantize_weight_128x128(x["b"])
+    dt, runs = _repeat_timed(lambda: o.grouped_gemm_contiguous(qa, sa, qb, sb, x["grouped_layout"]))
+    parts = parts_of(x["a"], x["b"], o.quantize_act_1x128,
+                     lambda qa, sa, qb, sb: o.grouped_gemm_contiguous(qa, sa, qb, sb, x["grouped_layout"]))
+    return result(w.flops, dt, runs, f"full steps of {w.name} (fp64 dequantize + matmul over all valid rows)", parts)
 
 
 def quant_bytes(G, M, K, in_size):
@@ -308,6 +385,100 @@ def bench_quant(args):
         torch.cuda.synchronize(dev)
 
 
+def graph_cross_check(args, calls, sets, w, dev):
+    """The second timing of the page-3 protocol (section "Measurement"): a
+    hipGraph that holds graph_launches launches (the same rotating input sets),
+    replayed, timed with HIP events on the replay stream and divided by the
+    launches.  The output of input set 0 after the replays must equal, bit for
+    bit, that of an eager launch on the same inputs."""
+    import torch
+    import fp8_block_scaled_amd as gfg
+    n = args.graph_launches
+    s = torch.cuda.Stream(dev)
+    h = s.cuda_stream
+    gcalls = [(fn, a[:-1] + (h,)) for fn, a in calls]
+
+    def launch(i):
+        fn, a = gcalls[i % len(gcalls)]
+        rc = fn(*a)
+        if rc:
+            raise gfg.GfgError(rc, gfg.load_library().grouped_fp8_last_error().decode())
+
+    torch.cuda.synchronize(dev)
+    with torch.cuda.stream(s):
+        launch(0)
+    torch.cuda.synchronize(dev)
+    eager = sets[0]["d"].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(n):
+            launch(i)
+    replays = max(3, args.steps // n)
+    with torch.cuda.stream(s):           # replay() launches on the current stream
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(s)
+        for _ in range(replays):
+            g.replay()
+        stop.record(s)
+    torch.cuda.synchronize(dev)
+    ms = start.elapsed_time(stop) / (replays * n)
+    same = bool(torch.equal(sets[0]["d"].view(torch.int16), eager.view(torch.int16)))
+    if not same:
+        raise RuntimeError("graph replay output differs from the eager launch")
+    return {"launches_per_graph": n, "replays": replays, "ms_per_launch": round(ms, 6),
+            "TFLOPs": round(w.flops / (ms * 1e-3) / 1e12, 3), "matches_eager_bitwise": same}
+
+
+def measure_ceilings(a_bytes, dev):
+    """The committed ceiling kernels, timed with HIP events on their stream:
+    the scaled MFMA alone on real E4M3 operands (the first bytes of the
+    workload's A), and a 1 GiB HBM copy."""
+    import torch
+    import fp8_block_scaled_amd as gfg
+    s = torch.cuda.Stream(dev)
+    h = s.cuda_stream
+    nb = gfg.ceiling_mfma_operand_bytes()
+    flat = a_bytes.reshape(-1).view(torch.uint8)
+    if flat.numel() < nb:
+        flat = flat.repeat(-(-nb // flat.numel()))
+    ops = flat[:nb].clone()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize(dev)
+
+    def timed(fn, reps):
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.synchronize(dev)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(s)
+        for _ in range(reps):
+            fn()
+        stop.record(s)
+        torch.cuda.synchronize(dev)
+        return start.elapsed_time(stop) / reps * 1e-3
+
+    iters = 4000
+    flops = [0.0]
+
+    def mfma():
+        flops[0] = gfg.ceiling_mfma(ops.data_ptr(), nb, iters, sink.data_ptr(), sink.numel(), h)
+
+    t_m = timed(mfma, 20)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    t_c = timed(lambda: gfg.ceiling_copy(src.data_ptr(), dst.data_ptr(), nbytes, h), 20)
+    del src, dst
+    return {"mfma_TFLOPs": round(flops[0] / t_m / 1e12, 1),
+            "mfma_kernel": f"gfg_ceiling_mfma, {iters} x 16 v_mfma_scale_f32_32x32x64_f8f6f4 per wave, 8 waves per CU",
+            "copy_GBps": round(2 * nbytes / t_c / 1e9, 1),
+            "copy_kernel": "gfg_ceiling_copy, 1 GiB, read + write bytes"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,7 +503,18 @@ def main():
                     help="output tile of the plain FP8 GEMM (auto: chosen per launch)")
     ap.add_argument("--num-xcd", type=int, default=8, help="XCDs the tile order is split over (1 or 8)")
     ap.add_argument("--group-m", type=int, default=0, help="grouped-M width in M tiles (0: kernel default)")
+    ap.add_argument("--graph-launches", type=int, default=20,
+                    help="cross-check: time a hipGraph of this many launches, replayed; 0 skips it")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured MFMA-only and copy ceilings")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print per-kernel durations (all dispatches and the final 100) of a rocprofv3 "
+                         "--kernel-trace csv run under DIR, then exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        for r in summarize_trace(args.trace_summary):
+            print(json.dumps(r))
+        return
     if args.op == "quant":
         if args.gpus != 1:
             raise SystemExit("this benchmark runs on one GPU only")
@@ -448,6 +630,9 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBS, 4), "traffic": traffic}
 
+    graph = graph_cross_check(args, calls, sets, w, dev) if args.graph_launches > 0 else None
+    ceilings = None if args.no_ceilings else measure_ceilings(sets[0]["a"], dev)
+
     res = {
         "metric": "grouped FP8 GEMM TFLOP/s (valid rows) and % of FP8 MFMA peak, 1 MI355X",
         "value": round(tflops, 3),
@@ -472,6 +657,11 @@ def main():
         "algorithmic_GBps": round(gbps, 1),
         "host_wall_s_timed": round(wall, 4),
     }
+    if graph:
+        res["graph_cross_check"] = graph
+    if ceilings:
+        ceilings["frac_of_mfma_ceiling"] = round(tflops / ceilings["mfma_TFLOPs"], 4)
+        res["ceilings"] = ceilings
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, x0)
     print(json.dumps(res), flush=True)

@@ -100,6 +100,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.grouped_fp8_set_tile_shape.restype = ctypes.c_int
     lib.grouped_fp8_set_grid_limit.argtypes = [i32]
     lib.grouped_fp8_set_grid_limit.restype = ctypes.c_int
+    lib.gfg_ceiling_mfma_operand_bytes.argtypes = []
+    lib.gfg_ceiling_mfma_operand_bytes.restype = i64
+    lib.gfg_ceiling_mfma.argtypes = [vp, i64, i32, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
+    lib.gfg_ceiling_mfma.restype = ctypes.c_int
+    lib.gfg_ceiling_copy.argtypes = [vp, vp, i64, vp]
+    lib.gfg_ceiling_copy.restype = ctypes.c_int
     lib.gfg_version.argtypes = []
     lib.gfg_version.restype = ctypes.c_char_p
     if path is None:
@@ -129,6 +135,25 @@ def set_tile_shape(shape: int = TILE_AUTO) -> None:
 def set_grid_limit(max_workgroups: int = 0) -> None:
     """Cap the workgroups of a GEMM launch (0: one per CU)."""
     _check(load_library().grouped_fp8_set_grid_limit(max_workgroups))
+
+
+# ------------------------------------------------------------------ measured ceilings
+def ceiling_mfma_operand_bytes() -> int:
+    return int(load_library().gfg_ceiling_mfma_operand_bytes())
+
+
+def ceiling_mfma(operands, operand_bytes, iters, sink, sink_floats, stream=0) -> float:
+    """Launch the scaled-MFMA ceiling kernel (device addresses); returns the
+    FLOPs of the launch."""
+    flops = ctypes.c_double(0.0)
+    _check(load_library().gfg_ceiling_mfma(operands, operand_bytes, iters, sink, sink_floats,
+                                           ctypes.byref(flops), stream))
+    return flops.value
+
+
+def ceiling_copy(src, dst, nbytes, stream=0) -> None:
+    """Launch the HBM copy ceiling kernel (device addresses)."""
+    _check(load_library().gfg_ceiling_copy(src, dst, nbytes, stream))
 
 
 # ------------------------------------------------------------------ raw pointer calls

@@ -30,23 +30,20 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-ar
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# The device sources, compiled one object each.
+HIP_SOURCES = ["gfg_gemm.hip", "gfg_gemm256.hip", "gfg_quant.hip", "gfg_ceiling.hip"]
+
+
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     out_dir = os.path.join(ROOT, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    objs = []
-    steps = [
-        [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "gfg_gemm.hip"),
-         "-o", os.path.join(out_dir, "gfg_gemm.o")],
-        [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "gfg_gemm256.hip"),
-         "-o", os.path.join(out_dir, "gfg_gemm256.o")],
-        [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, "gfg_quant.hip"),
-         "-o", os.path.join(out_dir, "gfg_quant.o")],
-        ["g++", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-pthread", "-I", INCLUDE, "-I", CSRC, "-c",
-         os.path.join(CSRC, "gfg_host.cpp"), "-o", os.path.join(out_dir, "gfg_host.o")],
-    ]
-    objs = [os.path.join(out_dir, "gfg_gemm.o"), os.path.join(out_dir, "gfg_gemm256.o"),
-            os.path.join(out_dir, "gfg_quant.o"), os.path.join(out_dir, "gfg_host.o")]
+    o = lambda n: os.path.join(out_dir, n)
+    steps = [[hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src),
+              "-o", o(src.replace(".hip", ".o"))] for src in HIP_SOURCES]
+    steps.append(["g++", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-pthread", "-I", INCLUDE, "-I", CSRC,
+                  "-c", os.path.join(CSRC, "gfg_host.cpp"), "-o", o("gfg_host.o")])
+    objs = [o(src.replace(".hip", ".o")) for src in HIP_SOURCES] + [o("gfg_host.o")]
     tmp = LIB + ".tmp"
     steps.append([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp])
     for cmd in steps:
@@ -85,17 +82,14 @@ def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:
     os.makedirs(out_dir, exist_ok=True)
     common = ["-O1", "-g", "-fno-omit-frame-pointer", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
     o = lambda n: os.path.join(out_dir, n)
-    steps = [
-        [hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
-         "-packed-fp32-ops", "-c", os.path.join(CSRC, "gfg_gemm.hip"), "-o", o("gfg_gemm.o")],
-        [hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
-         "-packed-fp32-ops", "-c", os.path.join(CSRC, "gfg_gemm256.hip"), "-o", o("gfg_gemm256.o")],
-        [hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
-         "-packed-fp32-ops", "-c", os.path.join(CSRC, "gfg_quant.hip"), "-o", o("gfg_quant.o")],
+    steps = [[hipcc, f"--offload-arch={ARCH}", *common, *SAN_HOST, "-Xclang", "-target-feature", "-Xclang",
+              "-packed-fp32-ops", "-c", os.path.join(CSRC, src), "-o", o(src.replace(".hip", ".o"))]
+             for src in HIP_SOURCES]
+    steps += [
         [clang, *common, "-pthread", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-c",
          os.path.join(CSRC, "gfg_host.cpp"), "-o", o("gfg_host.o")],
         [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *SAN_HOST[:4], "-shared-libasan",
-         o("gfg_gemm.o"), o("gfg_gemm256.o"), o("gfg_quant.o"), o("gfg_host.o"), "-o", o("libgfg_san.so")],
+         *[o(src.replace(".hip", ".o")) for src in HIP_SOURCES], o("gfg_host.o"), "-o", o("libgfg_san.so")],
     ]
     for cmd in steps:
         if verbose:

@@ -49,3 +49,37 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in line["error"]
+
+
+def test_trace_summary_final_100(tmp_path):
+    """bench.py --trace-summary: per-kernel calls, overall mean and the mean of
+    the final 100 dispatches by start time, from a rocprofv3 kernel-trace csv."""
+    import csv
+    rows = []
+    for i in range(250):                       # 250 GEMM dispatches: 1000 ns, last 100 at 500 ns
+        dur = 500 if i >= 150 else 1000
+        rows.append(("gemm_kernel", 10_000 * i, 10_000 * i + dur))
+    rows.append(("copy", 5, 25))
+    rows.reverse()                               # the file order must not matter
+    d = tmp_path / "run"
+    d.mkdir()
+    with open(d / "x_kernel_trace.csv", "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for name, t0, t1 in rows:
+            wr.writerow(["KERNEL_DISPATCH", name, t0, t1])
+    out = {r["kernel"]: r for r in bench.summarize_trace(str(tmp_path))}
+    g = out["gemm_kernel"]
+    assert g["calls"] == 250
+    assert g["final100_mean_ns"] == 500.0
+    assert g["mean_ns"] == (150 * 1000 + 100 * 500) / 250
+    assert out["copy"]["calls"] == 1 and out["copy"]["final100_mean_ns"] == 20.0
+
+
+def test_kernel_source_hash_ignores_comments(tmp_path):
+    a, b = tmp_path / "a.hip", tmp_path / "b.hip"
+    a.write_text("int x; // one\n\nint y;\n")
+    b.write_text("int x;   // two\nint y;\n")
+    assert bench.kernel_source_hash([str(a)]) == bench.kernel_source_hash([str(b)])
+    b.write_text("int x;\nint z;\n")
+    assert bench.kernel_source_hash([str(a)]) != bench.kernel_source_hash([str(b)])

@@ -1,0 +1,33 @@
+"""The measured-ceiling kernels the benchmark reports against: the copy
+kernel copies, and the MFMA kernel runs and reports its FLOPs."""
+import pytest
+import torch
+
+import fp8_block_scaled_amd as gfg
+
+pytestmark = pytest.mark.gpu
+
+
+def test_ceiling_copy_copies():
+    dev = torch.device("cuda:0")
+    n = (1 << 20) + 48
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev)
+    dst = torch.zeros_like(src)
+    gfg.ceiling_copy(src.data_ptr(), dst.data_ptr(), n)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
+def test_ceiling_mfma_runs_and_counts():
+    dev = torch.device("cuda:0")
+    nb = gfg.ceiling_mfma_operand_bytes()
+    ops = torch.full((nb,), 0x38, dtype=torch.uint8, device=dev)     # E4M3 1.0
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    flops = gfg.ceiling_mfma(ops.data_ptr(), nb, 3, sink.data_ptr(), sink.numel())
+    torch.cuda.synchronize()
+    assert flops == cus * 8 * 3 * 16 * 2 * 32 * 32 * 64
+    # every product is 1 * 1 with unit scales: each accumulator element sums
+    # 3 iterations x 2 K halves x 64 products, and a lane holds 8 x 16 of them
+    assert torch.all(sink == 3 * 2 * 64 * 128).item()
+

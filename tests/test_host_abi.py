@@ -422,3 +422,13 @@ def test_launch_settings_argument_errors():
     assert lib.grouped_fp8_set_tile_order(1, 4) == 0 and lib.grouped_fp8_set_tile_order(8, 0) == 0
     assert lib.grouped_fp8_set_tile_shape(2) == 0 and lib.grouped_fp8_set_tile_shape(0) == 0
     assert lib.grouped_fp8_set_grid_limit(16) == 0 and lib.grouped_fp8_set_grid_limit(0) == 0
+
+
+def test_ceiling_argument_errors():
+    """The ceiling kernels' host checks (no launch happens)."""
+    with pytest.raises(gfg.GfgError) as e:
+        gfg.ceiling_copy(16, 32, 17)
+    assert e.value.code == 1
+    with pytest.raises(gfg.GfgError) as e:
+        gfg.ceiling_mfma(32, 16, 1, 64, 1 << 20)
+    assert e.value.code == 1
