@@ -136,7 +136,8 @@ struct TileCtx {
     // returns zero for any offset past the count instead of touching memory.
     const uint8_t* a_tile;            // A row m0, K 0 of the region
     const uint8_t* b_tile;            // B row n0 of expert g, K 0
-    __amdgpu_buffer_rsrc_t sa_rsrc;   // scale_a from row m0 of K-block 0 to the region's end
+    const uint8_t* sa_base;           // scale_a row m0 of K-block 0 (of the region)
+    uint32_t sa_kbytes;               // bytes of one K step's scale_a rows from row m0 (sa_stride - m0)
     const uint8_t* sb_row;            // scale_b row (all K-blocks) of this wave's 128-column block
     const uint8_t* sbu_row;           // SILU: scale_b row of the up block (sb_row: the gate block)
     uint32_t sa_stride;        // scale_a bytes between 128-wide K steps
@@ -160,15 +161,23 @@ struct Frags {
     v8i b[BN / 64];
 };
 
+// The buffer resource of K step kb's scale_a rows from row m0: the range
+// check covers the lane's whole offset, so rows past the region's end read
+// zero in every K step instead of bytes past the tensor.
+template <class C>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sa_rsrc(const C& c, int kb) {
+    return make_rsrc(c.sa_base + uint64_t(uint32_t(kb)) * c.sa_stride, c.sa_kbytes);
+}
+
 // This lane's A-scale loads for stage kb (one dword, or FM bytes).
 template <class C>
 __device__ __forceinline__ void load_sa(const C& c, int kb, int (&sa)[4]) {
-    const uint32_t so = uint32_t(kb) * c.sa_stride;
+    const __amdgpu_buffer_rsrc_t rs = sa_rsrc(c, kb);
     if constexpr (C::SAW) {
-        sa[0] = int(__builtin_amdgcn_raw_buffer_load_b32(c.sa_rsrc, c.sa_off[0], so, 0));
+        sa[0] = int(__builtin_amdgcn_raw_buffer_load_b32(rs, c.sa_off[0], 0, 0));
     } else {
 #pragma unroll
-        for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(c.sa_rsrc, c.sa_off[f], so, 0);
+        for (int f = 0; f < C::FM; ++f) sa[f] = __builtin_amdgcn_raw_buffer_load_b8(rs, c.sa_off[f], 0, 0);
     }
 }
 
@@ -191,7 +200,7 @@ __device__ __forceinline__ void issue_stage(const C& c, GFG_LDS uint8_t* __restr
         sb = load_scale_word(c.sb_row, kb);
     if constexpr (C::SILU && !C::MX) sbu = load_scale_word(c.sbu_row, kb);
     if constexpr (C::MX4) {
-        sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(c.sa_rsrc, c.sa_off[1], uint32_t(kb) * c.sa_stride, 0));
+        sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(sa_rsrc(c, kb), c.sa_off[1], 0, 0));
         sbu = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off1, uint32_t(kb) * c.sb_stride, 0));
     }
     // K-block base pointers made opaque scalars, so each DMA address is a scalar
@@ -349,8 +358,7 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
             sb = load_scale_word(c.sb_row, kb_refill);
         if constexpr (C::SILU && !C::MX) sbu = load_scale_word(c.sbu_row, kb_refill);
         if constexpr (C::MX4) {
-            sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(c.sa_rsrc, c.sa_off[1], uint32_t(kb_refill) * c.sa_stride,
-                                                             0));
+            sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(sa_rsrc(c, kb_refill), c.sa_off[1], 0, 0));
             sbu = int(__builtin_amdgcn_raw_buffer_load_b32(c.sb_rsrc, c.sb_off1, uint32_t(kb_refill) * c.sb_stride,
                                                            0));
         }
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         C c;
         c.a_tile = a_reg + m0 * p.K;
         c.b_tile = p.b + (int64_t(g) * p.N + n0) * p.K;
-        c.sa_rsrc = make_rsrc(sa_reg + m0, uint32_t(int64_t(SKB) * p.rows - m0));
+        c.sa_base = uniform_ptr(sa_reg + m0);
         if constexpr (C::MX) {
             // scale_b [G][K/32][N]: this lane's dword holds rows n0 + wn*WN +
             // 4*l16 .. +3 of block 4*kb + lq (MX4: 8*kb + lq, and 8*kb + 4 + lq)
@@ -509,6 +517,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
             c.sb_row = uniform_ptr(p.b_scale + (int64_t(g) * NB + (n0 + wn * WN) / 128) * KB);
         }
         c.sa_stride = uint32_t((MX4 ? 8 : MX ? 4 : 1) * p.rows);
+        c.sa_kbytes = c.sa_stride - uint32_t(m0);
         // DMA chunk j of this wave fills LDS rows 8*(j*WAVES + wave) .. +7; lane i
         // writes physical chunk i%8 of tile row R = +i/8, which holds logical
         // chunk (i%8) ^ key(R) of that row (A: key (R >> 2) & 7, B: R & 7).
@@ -596,10 +605,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm_kernel(Params p)
         }
 
         // prologue: stages 0..2 in flight (clamped to the last stage), stage 0's
-        // fragments in `fa`
+        // fragments in `fa`.  The wait counts stage 1's and 2's operations as
+        // the only ones younger than stage 0's, so the scheduler must not mix
+        // the stages' loads (nor move the layout load among them): the
+        // barriers pin the issue order.
+        __builtin_amdgcn_sched_barrier(0);
         issue_stage(c, buf0, 0, wave, sa0, sb0, su0);
+        __builtin_amdgcn_sched_barrier(0);
         issue_stage(c, buf1, min(1, KB - 1), wave, sa1, sb1, su1);
+        __builtin_amdgcn_sched_barrier(0);
         issue_stage(c, buf2, min(2, KB - 1), wave, sa2, sb2, su2);
+        __builtin_amdgcn_sched_barrier(0);
         GFG_WAITCNT(2 * L, 15);
         __builtin_amdgcn_s_barrier();
         read_frags(c, buf0, fa);

@@ -429,10 +429,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
     // the hardware drops (a window of zero bytes; distinct offsets, so that
     // none is merged away) and the tile's layout rows; then stage 0's
     // fragments of K half 0
+    // (The wait below counts everything issued after stage 0's loads; the
+    // scheduler barriers keep that issue order.)
+    __builtin_amdgcn_sched_barrier(0);
     dma_stage(rf, L.off, buf0, 0, wave);
+    __builtin_amdgcn_sched_barrier(0);
     load_scales(rf, 0, int(p.rows), L.sa_off, sa[0], sbw[0], sbs[0]);
     dma_stage(rf, L.off, buf1, 1, wave);
     load_scales(rf, 1, int(p.rows), L.sa_off, sa[1], sbw[1], sbs[1]);
+    __builtin_amdgcn_sched_barrier(0);
     {
         const __amdgpu_buffer_rsrc_t none = make_rsrc(p.d, 0);
 #pragma unroll
@@ -443,6 +448,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
             lay = __builtin_amdgcn_raw_buffer_load_b128(mr_, uint32_t(L.sa_off) * 4u, 0, 0);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
     GFG_WAITCNT(2 * SL + DMA_OPS + Epi<MASKED>::OPS, 15);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
