@@ -117,11 +117,17 @@ def summarize_trace(root, last=100):
     if not files:
         raise SystemExit(f"no kernel_trace.csv under {root}")
     per = collections.defaultdict(list)
+    res = {}
     for f in files:
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
                 per[r["Kernel_Name"]].append((t0, t1 - t0))
+                # kernel resources as the trace records them (first dispatch)
+                res.setdefault(r["Kernel_Name"], {k: int(r[c]) for k, c in (
+                    ("lds_bytes", "LDS_Block_Size"), ("scratch_bytes", "Scratch_Size"), ("vgpr", "VGPR_Count"),
+                    ("agpr", "Accum_VGPR_Count"), ("sgpr", "SGPR_Count"), ("workgroup", "Workgroup_Size_X"),
+                    ("grid", "Grid_Size_X")) if c in r and r[c] not in ("", None)})
     out = []
     for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
         v.sort()
@@ -129,7 +135,8 @@ def summarize_trace(root, last=100):
         tail = d[-last:]
         out.append({"kernel": name, "calls": len(d), "mean_ns": round(float(d.mean()), 1),
                     f"final{last}_mean_ns": round(float(tail.mean()), 1), f"final{last}_min_ns": int(tail.min()),
-                    f"final{last}_max_ns": int(tail.max()), f"final{last}_std_ns": round(float(tail.std()), 1)})
+                    f"final{last}_max_ns": int(tail.max()), f"final{last}_std_ns": round(float(tail.std()), 1),
+                    "resources": res.get(name, {})})
     return out
 
 
@@ -473,7 +480,10 @@ def measure_ceilings(a_bytes, dev):
     dst = torch.empty_like(src)
     t_c = timed(lambda: gfg.ceiling_copy(src.data_ptr(), dst.data_ptr(), nbytes, h), 20)
     del src, dst
-    return {"mfma_TFLOPs": round(flops[0] / t_m / 1e12, 1),
+    peak = gfg.device_peak()
+    return {"device_peak_TFLOPs": round(peak["fp8_tflops"], 1), "device_cus": peak["cus"],
+            "device_max_sclk_MHz": peak["max_sclk_mhz"],
+            "mfma_TFLOPs": round(flops[0] / t_m / 1e12, 1),
             "mfma_kernel": f"gfg_ceiling_mfma, {iters} x 16 v_mfma_scale_f32_32x32x64_f8f6f4 per wave, 8 waves per CU",
             "copy_GBps": round(2 * nbytes / t_c / 1e9, 1),
             "copy_kernel": "gfg_ceiling_copy, 1 GiB, read + write bytes"}
@@ -661,6 +671,7 @@ def main():
         res["graph_cross_check"] = graph
     if ceilings:
         ceilings["frac_of_mfma_ceiling"] = round(tflops / ceilings["mfma_TFLOPs"], 4)
+        ceilings["frac_of_device_peak"] = round(tflops / ceilings["device_peak_TFLOPs"], 4)
         res["ceilings"] = ceilings
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, x0)

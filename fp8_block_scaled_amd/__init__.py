@@ -100,6 +100,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.grouped_fp8_set_tile_shape.restype = ctypes.c_int
     lib.grouped_fp8_set_grid_limit.argtypes = [i32]
     lib.grouped_fp8_set_grid_limit.restype = ctypes.c_int
+    lib.gfg_device_peak.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int32)]
+    lib.gfg_device_peak.restype = ctypes.c_int
     lib.gfg_ceiling_mfma_operand_bytes.argtypes = []
     lib.gfg_ceiling_mfma_operand_bytes.restype = i64
     lib.gfg_ceiling_mfma.argtypes = [vp, i64, i32, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
@@ -138,6 +141,13 @@ def set_grid_limit(max_workgroups: int = 0) -> None:
 
 
 # ------------------------------------------------------------------ measured ceilings
+def device_peak() -> dict:
+    """The dense FP8 MFMA peak from the device's CU count and maximum clock."""
+    tf, cus, mhz = ctypes.c_double(0.0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load_library().gfg_device_peak(ctypes.byref(tf), ctypes.byref(cus), ctypes.byref(mhz)))
+    return {"fp8_tflops": tf.value, "cus": cus.value, "max_sclk_mhz": mhz.value}
+
+
 def ceiling_mfma_operand_bytes() -> int:
     return int(load_library().gfg_ceiling_mfma_operand_bytes())
 

@@ -70,6 +70,22 @@ using namespace gfg;
 
 extern "C" {
 
+GFG_API int gfg_device_peak(double* fp8_tflops, int32_t* cus, int32_t* max_sclk_mhz) {
+    clear_error();
+    if (!fp8_tflops || !cus || !max_sclk_mhz) return fail(GFG_EINVAL, "gfg_device_peak: null pointer argument");
+    int dev = 0, n = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(GFG_EHIP, "gfg_device_peak: hipGetDevice failed");
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev) != hipSuccess || n <= 0 || khz <= 0)
+        return fail(GFG_EHIP, "gfg_device_peak: hipDeviceGetAttribute failed");
+    *cus = n;
+    *max_sclk_mhz = khz / 1000;
+    // dense FP8 MFMA: per CU and clock, 4 SIMDs x 2048 FLOP (one 16x16x128 FP8
+    // MFMA, 65,536 FLOP, every 32 cycles per SIMD)
+    *fp8_tflops = double(n) * 8192.0 * double(khz) * 1e3 / 1e12;
+    return GFG_OK;
+}
+
 GFG_API int64_t gfg_ceiling_mfma_operand_bytes(void) {
     return int64_t(CEIL_THREADS / 64) * CEIL_FRAGS * 64 * 32;
 }

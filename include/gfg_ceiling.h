@@ -23,6 +23,15 @@
 extern "C" {
 #endif
 
+/*
+ * The dense FP8 MFMA peak derived from the current device's own CU count and
+ * maximum shader clock (hipDeviceAttributeClockRate): CUs x 8192 FLOP per
+ * clock (4 SIMDs, each one 16x16x128 FP8 MFMA of 65,536 FLOP per 32 cycles).
+ * All outputs are host pointers; null: GFG_EINVAL; a HIP query failing:
+ * GFG_EHIP.
+ */
+GFG_API int gfg_device_peak(double* fp8_tflops, int32_t* cus, int32_t* max_sclk_mhz);
+
 /* Bytes of operand data gfg_ceiling_mfma reads (device memory, 32-byte aligned). */
 GFG_API int64_t gfg_ceiling_mfma_operand_bytes(void);
 

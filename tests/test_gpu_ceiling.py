@@ -31,3 +31,12 @@ def test_ceiling_mfma_runs_and_counts():
     # 3 iterations x 2 K halves x 64 products, and a lane holds 8 x 16 of them
     assert torch.all(sink == 3 * 2 * 64 * 128).item()
 
+
+
+def test_device_peak_matches_device_properties():
+    """CUs x 8192 FP8 FLOP per clock at the device's maximum shader clock."""
+    props = torch.cuda.get_device_properties(0)
+    p = gfg.device_peak()
+    assert p["cus"] == props.multi_processor_count
+    assert 1000 <= p["max_sclk_mhz"] <= 3000
+    assert p["fp8_tflops"] == pytest.approx(p["cus"] * 8192 * p["max_sclk_mhz"] * 1e6 / 1e12, rel=1e-3)

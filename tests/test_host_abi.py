@@ -432,3 +432,5 @@ def test_ceiling_argument_errors():
     with pytest.raises(gfg.GfgError) as e:
         gfg.ceiling_mfma(32, 16, 1, 64, 1 << 20)
     assert e.value.code == 1
+    lib = gfg.load_library()
+    assert lib.gfg_device_peak(None, None, None) == 1
