@@ -442,7 +442,7 @@ def graph_cross_check(args, calls, sets, w, dev):
 def measure_ceilings(a_bytes, dev):
     """The committed ceiling kernels, timed with HIP events on their stream:
     the scaled MFMA alone on real E4M3 operands (the first bytes of the
-    workload's A), and a 1 GiB HBM copy."""
+    workload's A), a 1 GiB HBM copy and a 1 GiB HBM read."""
     import torch
     import fp8_block_scaled_amd as gfg
     s = torch.cuda.Stream(dev)
@@ -479,6 +479,8 @@ def measure_ceilings(a_bytes, dev):
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     t_c = timed(lambda: gfg.ceiling_copy(src.data_ptr(), dst.data_ptr(), nbytes, h), 20)
+    rsink = torch.empty(cus * 64, dtype=torch.int32, device=dev)
+    t_r = timed(lambda: gfg.ceiling_read(dst.data_ptr(), nbytes, rsink.data_ptr(), rsink.numel(), h), 20)
     del src, dst
     peak = gfg.device_peak()
     return {"device_peak_TFLOPs": round(peak["fp8_tflops"], 1), "device_cus": peak["cus"],
@@ -486,7 +488,9 @@ def measure_ceilings(a_bytes, dev):
             "mfma_TFLOPs": round(flops[0] / t_m / 1e12, 1),
             "mfma_kernel": f"gfg_ceiling_mfma, {iters} x 16 v_mfma_scale_f32_32x32x64_f8f6f4 per wave, 8 waves per CU",
             "copy_GBps": round(2 * nbytes / t_c / 1e9, 1),
-            "copy_kernel": "gfg_ceiling_copy, 1 GiB, read + write bytes"}
+            "copy_kernel": "gfg_ceiling_copy, 1 GiB, read + write bytes",
+            "read_GBps": round(nbytes / t_r / 1e9, 1),
+            "read_kernel": "gfg_ceiling_read, 1 GiB, non-temporal 16-byte loads"}
 
 
 def main():
@@ -516,7 +520,7 @@ def main():
     ap.add_argument("--graph-launches", type=int, default=20,
                     help="cross-check: time a hipGraph of this many launches, replayed; 0 skips it")
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the measured MFMA-only and copy ceilings")
+                    help="skip the measured MFMA-only, copy and read ceilings")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print per-kernel durations (all dispatches and the final 100) of a rocprofv3 "
                          "--kernel-trace csv run under DIR, then exit")
@@ -670,8 +674,17 @@ def main():
     if graph:
         res["graph_cross_check"] = graph
     if ceilings:
-        ceilings["frac_of_mfma_ceiling"] = round(tflops / ceilings["mfma_TFLOPs"], 4)
-        ceilings["frac_of_device_peak"] = round(tflops / ceilings["device_peak_TFLOPs"], 4)
+        if w.op in ("mx4", "mx4_silu"):
+            # the ceiling kernel and the device peak are FP8's; an FP4 MFMA of the
+            # same shape holds the matrix pipe half as long
+            ceilings["frac_of_device_peak"] = round(tflops / (2 * ceilings["device_peak_TFLOPs"]), 4)
+            ceilings["frac_of_mfma_ceiling"] = None
+        else:
+            ceilings["frac_of_mfma_ceiling"] = round(tflops / ceilings["mfma_TFLOPs"], 4)
+            ceilings["frac_of_device_peak"] = round(tflops / ceilings["device_peak_TFLOPs"], 4)
+        if roofline["bound"] == "hbm":     # algorithmic bytes against the measured memory rates
+            ceilings["frac_of_read_ceiling"] = round(gbps / ceilings["read_GBps"], 4)
+            ceilings["frac_of_copy_ceiling"] = round(gbps / ceilings["copy_GBps"], 4)
         res["ceilings"] = ceilings
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, x0)

@@ -109,6 +109,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.gfg_ceiling_mfma.restype = ctypes.c_int
     lib.gfg_ceiling_copy.argtypes = [vp, vp, i64, vp]
     lib.gfg_ceiling_copy.restype = ctypes.c_int
+    lib.gfg_ceiling_read.argtypes = [vp, i64, vp, i64, vp]
+    lib.gfg_ceiling_read.restype = ctypes.c_int
     lib.gfg_version.argtypes = []
     lib.gfg_version.restype = ctypes.c_char_p
     if path is None:
@@ -164,6 +166,12 @@ def ceiling_mfma(operands, operand_bytes, iters, sink, sink_floats, stream=0) ->
 def ceiling_copy(src, dst, nbytes, stream=0) -> None:
     """Launch the HBM copy ceiling kernel (device addresses)."""
     _check(load_library().gfg_ceiling_copy(src, dst, nbytes, stream))
+
+
+def ceiling_read(src, nbytes, sink, sink_words, stream=0) -> None:
+    """Launch the HBM read ceiling kernel (device addresses; sink: uint32 words,
+    at least CUs * 64)."""
+    _check(load_library().gfg_ceiling_read(src, nbytes, sink, sink_words, stream))
 
 
 # ------------------------------------------------------------------ raw pointer calls

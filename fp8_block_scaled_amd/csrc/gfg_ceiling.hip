@@ -1,7 +1,7 @@
 // Measured ceilings for the benchmark (gfx950): the rate of the GEMM's scaled
-// MFMA with nothing else running, and the rate of a plain HBM copy.  They are
-// not part of the GEMM; the benchmark reports its kernels' fractions against
-// these next to the published peaks.
+// MFMA with nothing else running, and the rates of a plain HBM copy and of a
+// plain HBM read.  They are not part of the GEMM; the benchmark reports its
+// kernels' fractions against these next to the published peaks.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -61,6 +61,27 @@ __global__ __launch_bounds__(256) void copy_ceiling_kernel(const u32x4* __restri
                                                            int64_t n) {
     const int64_t stride = int64_t(gridDim.x) * blockDim.x;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// Grid-stride read of n 16-byte words, four loads in flight per thread; each
+// wave writes the XOR of everything it read to sink[4 * block + wave].
+__global__ __launch_bounds__(256) void read_ceiling_kernel(const u32x4* __restrict__ src, int64_t n,
+                                                           uint32_t* __restrict__ sink) {
+    const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(src + i);
+        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        x ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n; i += stride) x ^= __builtin_nontemporal_load(src + i);
+    uint32_t v = x[0] ^ x[1] ^ x[2] ^ x[3];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) v ^= uint32_t(__shfl_xor(int(v), d, 64));
+    if ((threadIdx.x & 63) == 0) sink[int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)] = v;
 }
 
 }  // namespace
@@ -126,6 +147,24 @@ GFG_API int gfg_ceiling_copy(const void* src, void* dst, int64_t bytes, void* st
                        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(GFG_EHIP, "gfg_ceiling_copy: launch failed: %s", hipGetErrorString(e));
+    return GFG_OK;
+}
+
+GFG_API int gfg_ceiling_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words, void* stream) {
+    clear_error();
+    if (!src || !sink) return fail(GFG_EINVAL, "gfg_ceiling_read: null pointer argument");
+    if (bytes <= 0 || bytes % 16 != 0)
+        return fail(GFG_EINVAL, "gfg_ceiling_read: bytes=%lld must be a positive multiple of 16", (long long)bytes);
+    if (reinterpret_cast<uintptr_t>(src) & 15) return fail(GFG_EINVAL, "gfg_ceiling_read: src must be 16-byte aligned");
+    int cus = 0;
+    if (int rc = device_cus(&cus)) return rc;
+    if (sink_words < int64_t(cus) * 64)
+        return fail(GFG_EINVAL, "gfg_ceiling_read: sink holds %lld words, need %lld", (long long)sink_words,
+                    (long long)(int64_t(cus) * 64));
+    hipLaunchKernelGGL(read_ceiling_kernel, dim3(cus * 16), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(GFG_EHIP, "gfg_ceiling_read: launch failed: %s", hipGetErrorString(e));
     return GFG_OK;
 }
 

@@ -1,7 +1,7 @@
 /*
  * gfg_ceiling.h — measured ceilings of libgfg's benchmark (gfx950, MI355X).
  *
- * Not part of the grouped GEMM.  The benchmark times these two kernels on the
+ * Not part of the grouped GEMM.  The benchmark times these kernels on the
  * same GPU, in the same process, and reports its GEMM's fraction of each next
  * to the published peaks (FP8 dense MFMA 5.0 PFLOP/s, HBM 8 TB/s).  The second
  * reference page ("[Kernel][MI350] Add cache-aware 8-wave BF16/FP16 GEMM",
@@ -61,6 +61,19 @@ GFG_API int gfg_ceiling_mfma(const uint8_t* operands, int64_t operand_bytes, int
  * caches.
  */
 GFG_API int gfg_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/*
+ * The HBM read ceiling: reads src[0, bytes) with 16-byte non-temporal loads
+ * (16 workgroups of 256 threads per CU, grid-stride, four loads in flight per
+ * thread) and writes, per wave, the XOR of the 32-bit words it read to
+ * sink[4 * workgroup + wave], so sink's XOR is the XOR of all of src's words.
+ * src: device, 16-byte aligned; bytes a positive multiple of 16; sink: device
+ * uint32_t[sink_words], at least CUs * 64 words; else GFG_EINVAL.  A launch
+ * reads `bytes` from HBM when src exceeds the caches.  The ceiling for the
+ * read-dominated launches (weights streamed once), where the copy's equal
+ * mix of reads and writes is the wrong yardstick.
+ */
+GFG_API int gfg_ceiling_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
 """The measured-ceiling kernels the benchmark reports against: the copy
 kernel copies, and the MFMA kernel runs and reports its FLOPs."""
+import numpy as np
 import pytest
 import torch
 
@@ -16,6 +17,20 @@ def test_ceiling_copy_copies():
     gfg.ceiling_copy(src.data_ptr(), dst.data_ptr(), n)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def test_ceiling_read_reads_every_word():
+    """The XOR of the per-wave sinks is the XOR of every 32-bit word read."""
+    dev = torch.device("cuda:0")
+    n = (3 << 20) + 16 * 5                     # a ragged tail past the unrolled loop
+    src = torch.randint(-2**31, 2**31 - 1, (n // 4,), dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.full((cus * 64,), -1, dtype=torch.int32, device=dev)
+    gfg.ceiling_read(src.data_ptr(), n, sink.data_ptr(), sink.numel())
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
 
 
 def test_ceiling_mfma_runs_and_counts():

@@ -432,5 +432,11 @@ def test_ceiling_argument_errors():
     with pytest.raises(gfg.GfgError) as e:
         gfg.ceiling_mfma(32, 16, 1, 64, 1 << 20)
     assert e.value.code == 1
+    with pytest.raises(gfg.GfgError) as e:
+        gfg.ceiling_read(16, 24, 64, 1 << 20)          # bytes not a multiple of 16
+    assert e.value.code == 1
+    with pytest.raises(gfg.GfgError) as e:
+        gfg.ceiling_read(8, 32, 64, 1 << 20)           # src not 16-byte aligned
+    assert e.value.code == 1
     lib = gfg.load_library()
     assert lib.gfg_device_peak(None, None, None) == 1
