@@ -441,8 +441,9 @@ def graph_cross_check(args, calls, sets, w, dev):
 
 def measure_ceilings(a_bytes, dev):
     """The committed ceiling kernels, timed with HIP events on their stream:
-    the scaled MFMA alone on real E4M3 operands (the first bytes of the
-    workload's A), a 1 GiB HBM copy and a 1 GiB HBM read."""
+    the two scaled MFMAs alone on real E4M3 operands (the first bytes of the
+    workload's A; the faster one is the ceiling), a 1 GiB HBM copy and a
+    1 GiB HBM read."""
     import torch
     import fp8_block_scaled_amd as gfg
     s = torch.cuda.Stream(dev)
@@ -475,6 +476,12 @@ def measure_ceilings(a_bytes, dev):
         flops[0] = gfg.ceiling_mfma(ops.data_ptr(), nb, iters, sink.data_ptr(), sink.numel(), h)
 
     t_m = timed(mfma, 20)
+    flops16 = [0.0]
+
+    def mfma16():
+        flops16[0] = gfg.ceiling_mfma_16x16x128(ops.data_ptr(), nb, iters, sink.data_ptr(), sink.numel(), h)
+
+    t_m16 = timed(mfma16, 20)
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
@@ -485,8 +492,12 @@ def measure_ceilings(a_bytes, dev):
     peak = gfg.device_peak()
     return {"device_peak_TFLOPs": round(peak["fp8_tflops"], 1), "device_cus": peak["cus"],
             "device_max_sclk_MHz": peak["max_sclk_mhz"],
-            "mfma_TFLOPs": round(flops[0] / t_m / 1e12, 1),
-            "mfma_kernel": f"gfg_ceiling_mfma, {iters} x 16 v_mfma_scale_f32_32x32x64_f8f6f4 per wave, 8 waves per CU",
+            "mfma_TFLOPs": round(max(flops[0] / t_m, flops16[0] / t_m16) / 1e12, 1),
+            "mfma_32x32x64_TFLOPs": round(flops[0] / t_m / 1e12, 1),
+            "mfma_16x16x128_TFLOPs": round(flops16[0] / t_m16 / 1e12, 1),
+            "mfma_kernel": f"the faster of gfg_ceiling_mfma ({iters} x 16 v_mfma_scale_f32_32x32x64_f8f6f4 per wave) "
+                           f"and gfg_ceiling_mfma_16x16x128 ({iters} x 32 v_mfma_scale_f32_16x16x128_f8f6f4 per wave), "
+                           "8 waves per CU",
             "copy_GBps": round(2 * nbytes / t_c / 1e9, 1),
             "copy_kernel": "gfg_ceiling_copy, 1 GiB, read + write bytes",
             "read_GBps": round(nbytes / t_r / 1e9, 1),

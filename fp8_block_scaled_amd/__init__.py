@@ -107,6 +107,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.gfg_ceiling_mfma_operand_bytes.restype = i64
     lib.gfg_ceiling_mfma.argtypes = [vp, i64, i32, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
     lib.gfg_ceiling_mfma.restype = ctypes.c_int
+    lib.gfg_ceiling_mfma_16x16x128.argtypes = [vp, i64, i32, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
+    lib.gfg_ceiling_mfma_16x16x128.restype = ctypes.c_int
     lib.gfg_ceiling_copy.argtypes = [vp, vp, i64, vp]
     lib.gfg_ceiling_copy.restype = ctypes.c_int
     lib.gfg_ceiling_read.argtypes = [vp, i64, vp, i64, vp]
@@ -160,6 +162,15 @@ def ceiling_mfma(operands, operand_bytes, iters, sink, sink_floats, stream=0) ->
     flops = ctypes.c_double(0.0)
     _check(load_library().gfg_ceiling_mfma(operands, operand_bytes, iters, sink, sink_floats,
                                            ctypes.byref(flops), stream))
+    return flops.value
+
+
+def ceiling_mfma_16x16x128(operands, operand_bytes, iters, sink, sink_floats, stream=0) -> float:
+    """Launch the 16x16x128 scaled-MFMA ceiling kernel (device addresses);
+    returns the FLOPs of the launch."""
+    flops = ctypes.c_double(0.0)
+    _check(load_library().gfg_ceiling_mfma_16x16x128(operands, operand_bytes, iters, sink, sink_floats,
+                                                     ctypes.byref(flops), stream))
     return flops.value
 
 

@@ -1,5 +1,5 @@
-// Measured ceilings for the benchmark (gfx950): the rate of the GEMM's scaled
-// MFMA with nothing else running, and the rates of a plain HBM copy and of a
+// Measured ceilings for the benchmark (gfx950): the rates of the GEMM kernels'
+// two scaled MFMAs with nothing else running, and the rates of a plain HBM copy and of a
 // plain HBM read.  They are not part of the GEMM; the benchmark reports its
 // kernels' fractions against these next to the published peaks.
 #include <hip/hip_runtime.h>
@@ -53,6 +53,41 @@ __global__ __launch_bounds__(CEIL_THREADS, 1) void mfma_ceiling_kernel(const uin
         for (int x = 0; x < 2; ++x)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s += acc[y][x][i];
+    sink[size_t(blockIdx.x) * CEIL_THREADS + threadIdx.x] = s;
+}
+
+// The same operands, FLOPs and waves with v_mfma_scale_f32_16x16x128_f8f6f4
+// (the 128-row GEMM kernel's instruction): per iteration each wave issues 32 of
+// them, A fragments 0..3 against B fragments 4..11, on 32 four-register
+// accumulators.
+__global__ __launch_bounds__(CEIL_THREADS, 1) void mfma16_ceiling_kernel(const uint8_t* __restrict__ ops, int iters,
+                                                                         float* __restrict__ sink) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const v8i* src = reinterpret_cast<const v8i*>(ops) + size_t(wave) * CEIL_FRAGS * 64 + lane;
+    v8i f[CEIL_FRAGS];
+#pragma unroll
+    for (int j = 0; j < CEIL_FRAGS; ++j) f[j] = src[j * 64];
+    v4f acc[4][8];
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[y][x] = v4f{};
+    const int sc = 0x7f7f7f7f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+                acc[y][x] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f[4 + x], f[y], acc[y][x], 0, 0, 0, sc, 0,
+                                                                             sc);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s += acc[y][x][i];
     sink[size_t(blockIdx.x) * CEIL_THREADS + threadIdx.x] = s;
 }
 
@@ -131,6 +166,30 @@ GFG_API int gfg_ceiling_mfma(const uint8_t* operands, int64_t operand_bytes, int
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(GFG_EHIP, "gfg_ceiling_mfma: launch failed: %s", hipGetErrorString(e));
     *flops = double(cus) * (CEIL_THREADS / 64) * double(iters) * 16.0 * (32.0 * 32.0 * 64.0 * 2.0);
+    return GFG_OK;
+}
+
+GFG_API int gfg_ceiling_mfma_16x16x128(const uint8_t* operands, int64_t operand_bytes, int32_t iters, float* sink,
+                                        int64_t sink_floats, double* flops, void* stream) {
+    clear_error();
+    if (!operands || !sink || !flops) return fail(GFG_EINVAL, "gfg_ceiling_mfma_16x16x128: null pointer argument");
+    if (operand_bytes < gfg_ceiling_mfma_operand_bytes())
+        return fail(GFG_EINVAL, "gfg_ceiling_mfma_16x16x128: operands hold %lld bytes, need %lld",
+                    (long long)operand_bytes, (long long)gfg_ceiling_mfma_operand_bytes());
+    if (reinterpret_cast<uintptr_t>(operands) & 31)
+        return fail(GFG_EINVAL, "gfg_ceiling_mfma_16x16x128: operands must be 32-byte aligned");
+    if (iters < 1) return fail(GFG_EINVAL, "gfg_ceiling_mfma_16x16x128: iters=%d must be positive", iters);
+    int cus = 0;
+    if (int rc = device_cus(&cus)) return rc;
+    if (sink_floats < int64_t(cus) * CEIL_THREADS)
+        return fail(GFG_EINVAL, "gfg_ceiling_mfma_16x16x128: sink holds %lld floats, need %lld",
+                    (long long)sink_floats, (long long)(int64_t(cus) * CEIL_THREADS));
+    hipLaunchKernelGGL(mfma16_ceiling_kernel, dim3(cus), dim3(CEIL_THREADS), 0, static_cast<hipStream_t>(stream),
+                       operands, int(iters), sink);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(GFG_EHIP, "gfg_ceiling_mfma_16x16x128: launch failed: %s", hipGetErrorString(e));
+    *flops = double(cus) * (CEIL_THREADS / 64) * double(iters) * 32.0 * (16.0 * 16.0 * 128.0 * 2.0);
     return GFG_OK;
 }
 

@@ -55,3 +55,17 @@ def test_device_peak_matches_device_properties():
     assert p["cus"] == props.multi_processor_count
     assert 1000 <= p["max_sclk_mhz"] <= 3000
     assert p["fp8_tflops"] == pytest.approx(p["cus"] * 8192 * p["max_sclk_mhz"] * 1e6 / 1e12, rel=1e-3)
+
+
+def test_ceiling_mfma_16x16x128_runs_and_counts():
+    dev = torch.device("cuda:0")
+    nb = gfg.ceiling_mfma_operand_bytes()
+    ops = torch.full((nb,), 0x38, dtype=torch.uint8, device=dev)     # E4M3 1.0
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    flops = gfg.ceiling_mfma_16x16x128(ops.data_ptr(), nb, 3, sink.data_ptr(), sink.numel())
+    torch.cuda.synchronize()
+    assert flops == cus * 8 * 3 * 32 * 2 * 16 * 16 * 128
+    # each accumulator element sums 3 iterations x 128 products of 1 * 1, and
+    # a lane holds 32 x 4 of them
+    assert torch.all(sink == 3 * 128 * 128).item()

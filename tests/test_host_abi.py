@@ -433,6 +433,9 @@ def test_ceiling_argument_errors():
         gfg.ceiling_mfma(32, 16, 1, 64, 1 << 20)
     assert e.value.code == 1
     with pytest.raises(gfg.GfgError) as e:
+        gfg.ceiling_mfma_16x16x128(32, 16, 1, 64, 1 << 20)
+    assert e.value.code == 1
+    with pytest.raises(gfg.GfgError) as e:
         gfg.ceiling_read(16, 24, 64, 1 << 20)          # bytes not a multiple of 16
     assert e.value.code == 1
     with pytest.raises(gfg.GfgError) as e:
