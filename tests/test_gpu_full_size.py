@@ -15,6 +15,9 @@ weight draws, the rows of every expert that uses one draw.  Per chunk:
     unless the oracle's value itself is that number to within 1%;
   * the first chunk also checks that every padding / masked-off row of the
     whole output kept the sentinel, bit for bit.
+
+The five FP8 GEMM workloads run a second time with the other output tile
+(the one the automatic choice does not pick) forced, to the same checks.
 """
 import numpy as np
 import pytest
@@ -52,14 +55,15 @@ _ENTRY = {"gemm": gfg.grouped_fp8_gemm_contiguous,
 _run_cache = {}
 
 
-def _gpu_run(name):
-    """The workload's inputs, the library's bytes and the GPU output (cached:
-    the chunks of one workload share a single launch)."""
-    if name in _run_cache:
-        return _run_cache[name]
+def _gpu_run(name, tile=gfg.TILE_AUTO):
+    """The workload's inputs, the library's bytes and the GPU output with the
+    given tile shape (cached: the chunks of one workload share a single
+    launch)."""
+    if (name, tile) in _run_cache:
+        return _run_cache[(name, tile)]
     _run_cache.clear()
     w = wl.workload(name)
-    print(f"[full] launch {w.name} layout={w.layout} op={w.op} G={w.G} N={w.N} K={w.K}", flush=True)
+    print(f"[full] launch {w.name} layout={w.layout} op={w.op} G={w.G} N={w.N} K={w.K} tile={tile}", flush=True)
     x = wl.draw(w)
     qact, qw = _LIB_QUANT[w.op]
     if w.layout == "masked":
@@ -74,15 +78,19 @@ def _gpu_run(name):
     out_cols = w.I if w.op in ("silu_mul", "mx4_silu") else w.N
     shape = (w.G, w.M_max, out_cols) if w.layout == "masked" else (w.M, out_cols)
     d = torch.full(shape, SENTINEL, dtype=torch_dtype(w.out_dtype), device="cuda")
-    if w.layout == "masked":
-        gfg.grouped_fp8_gemm_masked(to_dev(qa), to_dev(sa), qb_d, sb_d, to_dev(x["masked_m"]), d)
-    else:
-        _ENTRY[w.op](to_dev(qa), to_dev(sa), qb_d, sb_d, to_dev(x["grouped_layout"]), d)
-    torch.cuda.synchronize()
+    gfg.set_tile_shape(tile)
+    try:
+        if w.layout == "masked":
+            gfg.grouped_fp8_gemm_masked(to_dev(qa), to_dev(sa), qb_d, sb_d, to_dev(x["masked_m"]), d)
+        else:
+            _ENTRY[w.op](to_dev(qa), to_dev(sa), qb_d, sb_d, to_dev(x["grouped_layout"]), d)
+        torch.cuda.synchronize()
+    finally:
+        gfg.set_tile_shape(gfg.TILE_AUTO)
     del qb_d, sb_d
     r = dict(w=w, x=x, qa=qa, sa=sa, qb=qb, sb=sb, bits=bits(d), got=d.float().cpu().numpy())
     del d
-    _run_cache[name] = r
+    _run_cache[(name, tile)] = r
     return r
 
 
@@ -107,12 +115,30 @@ def _no_stray_sentinel(b_rows, ref, out_dtype, what):
             f"{what}: {int(stray.sum())} valid outputs still hold the sentinel"
 
 
+# The FP8 workloads again with the tile shape the automatic choice does not
+# take, forced: the 256 x 256 kernel on the one-round, ragged and masked
+# shapes, the 128 x 256 kernel on the many-tile and long-K ones.
+_OTHER = {"contig_g4_m1024_n2048_k7168": gfg.TILE_256x256, "contig_g8_mrand_n7168_k2304": gfg.TILE_256x256,
+          "masked_g8_m1024_n2048_k7168": gfg.TILE_256x256,
+          "contig_g8_m4096_n7168_k2304_logmag": gfg.TILE_128x256, "dense_g1_m4096_n4096_k16384": gfg.TILE_128x256}
+_OTHER_CASES = [(n, c) for n in _OTHER for c in range(_chunks(wl.workload(n)))]
+
+
 @pytest.mark.parametrize("name,chunk", _CASES, ids=[f"{n}-{c}" for n, c in _CASES])
 def test_full_size_every_output(name, chunk):
-    r = _gpu_run(name)
+    _check_chunk(name, chunk, gfg.TILE_AUTO)
+
+
+@pytest.mark.parametrize("name,chunk", _OTHER_CASES, ids=[f"{n}-{c}" for n, c in _OTHER_CASES])
+def test_full_size_other_tile_shape(name, chunk):
+    _check_chunk(name, chunk, _OTHER[name])
+
+
+def _check_chunk(name, chunk, tile):
+    r = _gpu_run(name, tile)
     w, x = r["w"], r["x"]
     qact_o, qw_o = _ORACLE_QUANT[w.op]
-    what = f"{w.name} chunk {chunk}"
+    what = f"{w.name} tile {tile} chunk {chunk}"
     print(f"[full] {what}", flush=True)
     if w.layout == "masked":
         g, mm = chunk, int(x["masked_m"][chunk])
