@@ -1,5 +1,5 @@
 // Grouped FP8 (E4M3) block-scaled GEMM on 256 x 256 output tiles for gfx950
-// (MI355X): the launches with enough 256 x 256 tiles to give every CU one.
+// (MI355X): the launches with enough 256 x 256 tiles to keep every CU busy.
 //
 // Computes the same operation as the kernels of gfg_gemm.hip, the grouped GEMM
 // of the first reference page, "Grouped and Batched GEMM kernels with
@@ -14,20 +14,26 @@
 // 256 x 256 tile moves 64 KB for 16.8 MFLOP, a third less per FLOP.
 //
 // Design:
-//  * 8 wave64s, two per SIMD; wave w owns rows 128*(w >> 2) .. +127 and
-//    columns 64*(w & 3) .. +63 of the tile, so each SIMD holds one wave of
-//    each half of the rows;
-//  * v_mfma_scale_f32_32x32x64_f8f6f4 with the E8M0 bytes as hardware scale
-//    operands; a 128-K step is two 64-K halves, and the fragments of the next
-//    half are read from LDS while the current half's eight MFMAs run.  The
-//    four A fragments roll through four register slots (fragment y is
-//    replaced as soon as its two MFMAs are issued), the two B fragments are
-//    double-buffered: 128 accumulators plus 64 fragment registers;
-//  * two 64 KB LDS stages filled by direct-to-LDS loads; the LDS rows are
-//    stored fragment-major (row 32*y + p of a wave's A rows holds tile row
-//    4p + y, so a lane's four output rows are adjacent and share one A-scale
-//    dword), with 16-byte chunks XOR-swizzled by (row >> 1) & 7, which keeps
-//    both the fragment reads and the DMA writes free of bank conflicts;
+//  * 4 wave64s, one per SIMD, each owning a 128 x 128 quarter of the tile
+//    (rows 128*(w >> 1) .., columns 128*(w & 1) ..): 256 accumulator registers
+//    (64 16x16 blocks) and 192 fragment registers per wave.  Alone on its SIMD,
+//    a wave's instruction order is the schedule, so every group of
+//    instructions is pinned in place;
+//  * v_mfma_scale_f32_16x16x128_f8f6f4 with the E8M0 bytes as hardware scale
+//    operands: one instruction per 16 x 16 block and 128-K step, 64 per wave
+//    and step;
+//  * two 64 KB LDS stages filled by direct-to-LDS loads, A and B rows laid
+//    out alike: LDS row R holds tile row R ^ ((R >> 2) & 1), its 16-byte
+//    chunks XOR-swizzled by (R >> 2) & 7, so that a lane's four fragment rows
+//    (4 apart) share one A-scale dword and the fragment reads and DMA writes
+//    are free of bank conflicts;
+//  * two barriers per step: the first frees the B rows and half of the A rows
+//    of the stage just consumed, whose refill then starts under the first half
+//    of the step's MFMAs; the second (after stage k+1 has landed) frees the
+//    other A rows.  A wave's load instructions hold up its own MFMA issue, so
+//    spreading the step's 16 DMAs over both halves, instead of issuing them
+//    all in the second, cut the kernel time by 3 to 9% on the measured
+//    workloads;
 //  * a persistent grid over (M tile, N tile) work items in the shared
 //    XCD-range / grouped-M order; the refills of a tile's last two steps load
 //    the next tile's first two stages, and the tile's output stores are
@@ -35,12 +41,9 @@
 //    write stand between two tiles' MFMAs;
 //  * the contiguous layout's M tiles follow each expert's run of 128-row
 //    tiles in pairs (a run of odd length ends in a 128-row tile);
-//  * output through buffer stores of whole 128-byte lines: a 4 x 4 DPP
-//    transpose inside each lane quad turns the MFMA's (row, 16 columns) per
-//    lane into eight complete lines per store instruction, sent non-temporal
-//    (measured on the 32768 x 7168 x 2304 grouped case: partial-line stores
-//    cost about a fifth of the kernel time, whole-line temporal stores half
-//    of that, whole-line non-temporal ones a third of that again);
+//  * output through buffer stores of whole 128-byte lines: a DPP exchange
+//    between lane pairs turns the MFMA's (row, 4 x 4 columns) per lane into
+//    eight complete lines per store instruction, sent non-temporal;
 //  * a row that must stay untouched gets an offset past the store window,
 //    which the hardware drops, so every wave issues the same number of
 //    stores and the vector-memory waits stay exact.
@@ -56,22 +59,24 @@ namespace gfg {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int NTHREADS = 512, WAVES = 8;
+constexpr int NTHREADS = 256, WAVES = 4;
 constexpr int A_BYTES = BM * BK;                 // 32 KB of A per stage
 constexpr int STAGE = A_BYTES + BN * BK;         // + 32 KB of B
 constexpr int A_DMA = A_BYTES / 1024 / WAVES;    // 1 KB DMA instructions per wave and stage
 constexpr int B_DMA = BN * BK / 1024 / WAVES;
 constexpr int CAND_MAX = 4096;                   // candidate M tiles (128-row contiguous, 256-row masked)
-constexpr int FRAG_ROWS = 32 * BK;               // LDS bytes of one 32-row fragment
+constexpr int CPT = CAND_MAX / NTHREADS;         // candidates per thread in the list build
 
 // Vector-memory operations a wave issues, in order: per stage A_DMA + B_DMA
-// DMAs then one A-scale dword load; per tile boundary 16 output stores and,
-// for the contiguous layout, one load of the next tile's grouped_layout rows.
+// DMAs (FIRST_HALF_DMA of them before the step's mid barrier) then SL A-scale
+// dword loads; per tile boundary, for the contiguous layout, two loads of the
+// next tile's grouped_layout rows, then 32 output stores.
 constexpr int DMA_OPS = A_DMA + B_DMA;
-constexpr int SL = 1;
+constexpr int FIRST_HALF_DMA = 12;               // a step's DMAs issued before its mid-step barrier
+constexpr int SL = 2;                            // A-scale dwords per stage (two 64-row halves)
 template <bool MASKED>
 struct Epi {
-    static constexpr int OPS = 16 + (MASKED ? 0 : 1);
+    static constexpr int OPS = 32 + (MASKED ? 0 : 2);
 };
 
 // One work tile: contiguous: first 128-row candidate | (128 rows only) << 12 | expert << 16;
@@ -122,11 +127,11 @@ __device__ __forceinline__ Refill make_refill(const Params& p, const TileInfo& t
     r.a_rsrc = make_rsrc(p.a + (region + t.row0) * p.K, uint32_t(t.lim) * uint32_t(p.K));
     r.b_rsrc = make_rsrc(p.b + (int64_t(t.g) * p.N + t.n0) * p.K, uint32_t(BN) * uint32_t(p.K));
     r.sa_rsrc = make_rsrc(p.a_scale + region * KB + t.row0, uint32_t(int64_t(KB) * p.rows - t.row0));
-    r.sb_row = uniform_ptr(p.b_scale + (int64_t(t.g) * (p.N / 128) + (t.n0 + wn * 64) / 128) * KB);
+    r.sb_row = uniform_ptr(p.b_scale + (int64_t(t.g) * (p.N / 128) + t.n0 / 128 + wn) * KB);
     return r;
 }
 
-// Block-wide exclusive scan (sum, or max with identity -1) over the 512 threads.
+// Block-wide exclusive scan (sum, or max with identity -1) over the NTHREADS threads.
 template <bool MAX>
 __device__ __forceinline__ int block_exclusive_scan(int v, GFG_LDS int* tmp, int lane, int wave, int* total) {
     int x = v;
@@ -151,128 +156,236 @@ __device__ __forceinline__ int block_exclusive_scan(int v, GFG_LDS int* tmp, int
     return MAX ? max(pre, ex) : pre + ex;
 }
 
-// Issue one stage's loads: its A and B tiles by LDS DMA into `dst` and this
-// lane's scales (A: the dword of its four rows; B: the wave's scale word).
-// DMA chunk j of wave w fills LDS rows 8*(j*WAVES + w) .. +7 of A (then B);
-// lane i writes physical chunk i % 8 of row +i/8 from the offsets in off_a /
-// off_b (tile-invariant; the K step enters as the scalar offset).
+// LDS layout of a stage: 128-byte rows, A (256 rows) then B (256 rows), both
+// as the 128-row kernel's A tile: LDS row R holds tile row a_row(R) =
+// R ^ ((R >> 2) & 1) and its physical 16-byte chunk c the logical chunk
+// c ^ ((R >> 2) & 7).  A 16x16x128 fragment takes rows 4 apart (row
+// 64 h + 4 l16 + f of the wave's 128), so a lane's four rows share one
+// A-scale dword, and the row-parity exchange keeps the fragment reads free of
+// bank conflicts.  DMA chunk j of wave w fills LDS rows 8 (4 j + w) .. +7;
+// with four waves chunk j is chunk 0 moved by 32 j rows (a_row and the chunk
+// key do not depend on j).
+__device__ __forceinline__ int a_row(int p) { return p ^ ((p >> 2) & 1); }   // an involution
+__device__ __forceinline__ int swz_a(int p, int c) { return p * BK + ((c ^ ((p >> 2) & 7)) << 4); }
+
 struct LaneOffsets {
-    uint32_t a[A_DMA];
-    uint32_t b[B_DMA];
+    uint32_t a0;   // A chunk 0; chunk j adds 32 j rows
+    uint32_t b0;   // B chunk 0; chunk j adds 32 j rows
+    uint32_t K;    // row stride (uniform)
 };
+
+// DMA chunk c (0..15) of this wave for stage kb: chunks 0..7 are A's, 8..15 B's.
+__device__ __forceinline__ void dma_chunk(const Refill& r, LaneOffsets o, GFG_LDS uint8_t* dst, int kb, int wave,
+                                          int c) {
+    const uint32_t ks = uint32_t(kb) * BK;
+    asm volatile("" : "+v"(o.a0));   // re-added per chunk, not eight offsets held live
+    if (c < A_DMA) {
+        const int j = c;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r.a_rsrc, (GFG_LDS void*)(dst + (j * WAVES + wave) * 1024), 16,
+                                                 o.a0 + uint32_t(32 * j) * o.K, ks, 0, 0);
+    } else {
+        // every B row of a tile exists, so the chunk's row offset may go into
+        // the (unchecked) scalar offset
+        const int j = c - A_DMA;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r.b_rsrc, (GFG_LDS void*)(dst + A_BYTES + (j * WAVES + wave) * 1024),
+                                                 16, o.b0, ks + uint32_t(32 * j) * o.K, 0, 0);
+    }
+}
+
+// DMA chunk j (0..7) of this wave's B rows for stage kb, into the B region
+// `dst_b` of a stage buffer.
+__device__ __forceinline__ void dma_chunk_b(const Refill& r, LaneOffsets o, GFG_LDS uint8_t* dst_b, int kb, int wave,
+                                            int j) {
+    const uint32_t ks = uint32_t(kb) * BK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r.b_rsrc, (GFG_LDS void*)(dst_b + (j * WAVES + wave) * 1024), 16, o.b0,
+                                             ks + uint32_t(32 * j) * o.K, 0, 0);
+}
 
 __device__ __forceinline__ void dma_stage(const Refill& r, const LaneOffsets& o, GFG_LDS uint8_t* dst, int kb,
                                           int wave) {
-    const uint32_t ks = uint32_t(kb) * BK;
 #pragma unroll
-    for (int j = 0; j < A_DMA; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r.a_rsrc, (GFG_LDS void*)(dst + (j * WAVES + wave) * 1024), 16, o.a[j],
-                                                 ks, 0, 0);
-#pragma unroll
-    for (int j = 0; j < B_DMA; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r.b_rsrc,
-                                                 (GFG_LDS void*)(dst + A_BYTES + (j * WAVES + wave) * 1024), 16,
-                                                 o.b[j], ks, 0, 0);
+    for (int c = 0; c < DMA_OPS; ++c) dma_chunk(r, o, dst, kb, wave, c);
 }
 
-// (The K-block stride goes into the vector offset, which the hardware range
-// check covers: rows past the region's end in the last K-block read zero
-// instead of bytes past the tensor.)
-__device__ __forceinline__ void load_scales(const Refill& r, int kb, int rows, int sa_off, int& sa, int& sbw,
+// The lane's two A-scale dwords (rows 4 l16 .. +3 of each 64-row half of its
+// wave's rows) and the wave's B-scale word.  (The K-block stride goes into
+// the vector offset, which the hardware range check covers.)
+__device__ __forceinline__ void load_scales(const Refill& r, int kb, int rows, int sa_off, int (&sa)[2], int& sbw,
                                             int& sbs) {
-    sa = int(__builtin_amdgcn_raw_buffer_load_b32(r.sa_rsrc, uint32_t(sa_off) + uint32_t(kb) * uint32_t(rows), 0, 0));
+    const uint32_t kofs = uint32_t(kb) * uint32_t(rows);
+    sa[0] = int(__builtin_amdgcn_raw_buffer_load_b32(r.sa_rsrc, uint32_t(sa_off) + kofs, 0, 0));
+    sa[1] = int(__builtin_amdgcn_raw_buffer_load_b32(r.sa_rsrc, uint32_t(sa_off + 64) + kofs, 0, 0));
     sbw = load_scale_word(r.sb_row, kb);
     sbs = 8 * int((reinterpret_cast<uintptr_t>(r.sb_row) + uintptr_t(kb)) & 3);
 }
 
-__device__ __forceinline__ v8i read_frag(const GFG_LDS uint8_t* __restrict__ src, int a0, int a1) {
-    const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(src + a0);
-    const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(src + a1);
-    return __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
+// The lane index, read afresh where it is used: values derived from it ahead
+// of the tile loop would stay live (and be spilled) through the K loop.
+__device__ __forceinline__ int lane_now() {
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    return ln;
 }
 
-// Instruction order of one half step for the scheduler: MFMA (y, 0), a B
-// fragment read (two ds_read), [DMAs], MFMA (y, 1), A fragment y's two reads,
-// [DMAs]; the scale loads last.
-template <int Y, int NV>
-__device__ __forceinline__ void sched_half() {
-    if constexpr (Y < 4) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA (y, 0)
-        if constexpr (Y < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // B fragment read
-        if constexpr (NV > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // DMA
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA (y, 1)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                  // A fragment y
-        if constexpr (NV > 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // DMA
-        sched_half<Y + 1, NV>();
-    }
-}
-
-template <int Y>
-__device__ __forceinline__ void mfma_row(v16f (&acc)[4][2], const v8i (&bf)[2], const v8i& a, int sb, int sa) {
-    acc[Y][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[0], a, acc[Y][0], 0, 0, 0, sb, Y, sa);
-    acc[Y][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[1], a, acc[Y][1], 0, 0, 0, sb, Y, sa);
+// The lane's DMA source offset of chunk 0 (A and B alike), from the lane index
+// read afresh: computed per step, it is not held through the step's first half.
+// Chunk 0 of wave w covers LDS rows R = 8 w + (lane >> 3); lane i writes
+// physical chunk i % 8, the logical chunk (i % 8) ^ ((R >> 2) & 7) of tile row
+// a_row(R).
+__device__ __forceinline__ uint32_t dma_lane_offset(int wave, uint32_t K) {
+    const int ln = lane_now();
+    const int R = 8 * wave + (ln >> 3);
+    return uint32_t(a_row(R)) * K + uint32_t(((ln & 7) ^ ((R >> 2) & 7)) << 4);
 }
 
 struct Lane {
-    int a_addr[2][2];    // [K half][chunk] LDS offsets of this lane's A fragment reads (+ 4096 * y)
-    int b_addr[2][2];    // B (+ 4096 * x), from the stage base
+    // LDS offsets of this lane's fragment rows for the first 64-row half and
+    // fragment f = 0 (row p0 + odd for even f, p0 - odd for odd f, then + f
+    // rows); logical chunks lq (lo) and lq + 4 (hi).  The second half adds 64
+    // rows.  B offsets include the A region.
+    int a_lo_e, a_lo_o, a_hi_e, a_hi_o;
+    int b_lo_e, b_lo_o, b_hi_e, b_hi_o;
     LaneOffsets off;     // DMA source offsets
     int wave, wm, wn, sa_off;
 };
 
-// One 128-K step k: stage k in `cur`, stage k+1 in `nxt` (its DMA in flight
-// until this step's second half).  On entry af / bf0 hold the fragments of
-// (k, K half 0).  The first half runs their MFMAs and reads (k, half 1); the
-// second half waits for stage k+1 and the other waves, refills `cur` with
-// stage kr (k + 2 of this tile, or the next tile's stage, or a dummy copy of
-// the last stage when nothing is left), runs (k, half 1) and reads
-// (k+1, half 0) from `nxt`.  VMWAIT: vector-memory operations issued after
-// stage k+1's DMAs (its A-scale load, plus the tile-boundary operations in the
-// first step of a tile).  Both halves are straight-line code, so the
-// scheduler keeps the MFMA / fragment-read / DMA interleave.
-template <int PAR, int VMWAIT>
+__device__ __forceinline__ int frag_off(int e, int o, int y) {
+    const int f = y & 3;
+    return ((f & 1) ? o : e) + f * BK + (y >> 2) * 64 * BK;
+}
+
+#define GFG_SB() __builtin_amdgcn_sched_barrier(0)
+
+
+__device__ __forceinline__ u32x4 lds16(const GFG_LDS uint8_t* __restrict__ src, int a) {
+    return *reinterpret_cast<const GFG_LDS u32x4*>(src + a);
+}
+__device__ __forceinline__ v8i join(u32x4 l, u32x4 h) {
+    return __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ v4f mfma(const v8i& b, const v8i& a, const v4f& c, int sb, int y, int sa) {
+    switch (y & 3) {   // the A-scale byte (op_sel) must be a constant
+        case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, sb, 0, sa);
+        case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, sb, 1, sa);
+        case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, sb, 2, sa);
+        default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, sb, 3, sa);
+    }
+}
+
+// The row mask of a lane: bit y set when its output row for fragment y may be
+// written (inside the tile's rows and, for the contiguous layout, of the
+// tile's expert).
+template <bool MASKED>
+__device__ __forceinline__ int row_mask(const Lane& L, const u32x4 (&lay)[2], int lim, int g) {
+    int okm = 0;
+#pragma unroll
+    for (int y = 0; y < 8; ++y)
+        okm |= int(L.sa_off + 64 * (y >> 2) + (y & 3) < lim && (MASKED || int(lay[y >> 2][y & 3]) == g)) << y;
+    return okm;
+}
+
+// One 128-K step k: stage k in `cur` (its B region also as `cur_b`), stage
+// k+1 in `nxt`; 64 MFMAs per wave in row order.  On entry af[0..3] and bc hold
+// stage k's A fragments 0..3 and B fragments.
+//  * start barrier: every wave has read stage k's B and A 0..3 fragments, so
+//    their LDS rows (the B region and DMA chunks 0, 1, 4, 5 of A) are free;
+//  * first half (fragment rows 0..3): reads stage k's A fragments 4..7 into
+//    their slots over the first 8 MFMAs, then refills the free rows with
+//    stage kr, one DMA per two MFMAs (12 DMAs);
+//  * mid barrier: stage k+1 has landed and every wave has read stage k's
+//    A fragments 4..7;
+//  * second half (rows 4..7): reads stage k+1's B fragments into bn and its
+//    A fragments 0..3 into slots 0..3, and refills the last four A chunks.
+// VMWAIT counts the vector-memory operations issued after stage k+1's last
+// DMA: the A-scale loads of its step and this step's first-half DMAs, plus
+// the tile-boundary operations in the first step of a tile.  The DMAs of a
+// half follow its LDS reads of the same buffer: a read issued after a DMA
+// into the same buffer would make the compiler wait for the DMA.
+// FIRST: the first step of a tile also folds the tile's layout words into
+// the row mask right after its mid barrier, so they are not held through the
+// step pair.
+template <int PAR, int VMWAIT, bool MASKED = false, bool FIRST = false>
 __device__ __forceinline__ void k_step(const Lane& L, int rows, GFG_LDS uint8_t* __restrict__ cur,
-                                       GFG_LDS uint8_t* __restrict__ nxt, int kr, const Refill& rf,
-                                       v16f (&acc)[4][2], v8i (&af)[4], v8i (&bf0)[2], v8i (&bf1)[2], int (&sa)[2],
-                                       int (&sbw)[2], int (&sbs)[2]) {
-    const int sa_k = sa[PAR];
+                                       GFG_LDS uint8_t* __restrict__ cur_b, GFG_LDS uint8_t* __restrict__ nxt, int kr,
+                                       const Refill& rf,
+                                       v4f (&acc)[8][8], v8i (&af)[8], v8i (&bc)[8], v8i (&bn)[8],
+                                       int (&sa)[2][2], int (&sbw)[2], int (&sbs)[2], GFG_LDS uint8_t* okm = nullptr,
+                                       const u32x4* lay = nullptr, int lim = 0, int g = 0) {
     const int sb_k = (sbw[PAR] >> sbs[PAR]) & 0xff;
-    // ---- K half 0
-    __builtin_amdgcn_sched_barrier(0);
+    const int sa0 = sa[PAR][0], sa1 = sa[PAR][1];
+    // ---- start barrier: every wave's reads of stage k's B and A 0..3
+    // fragments (issued in the previous step's second half) have completed
+    GFG_SB();
     GFG_WAITCNT(63, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_row<0>(acc, bf0, af[0], sb_k, sa_k);
-    bf1[0] = read_frag(cur, L.b_addr[1][0], L.b_addr[1][1]);
-    af[0] = read_frag(cur, L.a_addr[1][0], L.a_addr[1][1]);
-    mfma_row<1>(acc, bf0, af[1], sb_k, sa_k);
-    bf1[1] = read_frag(cur, L.b_addr[1][0] + FRAG_ROWS, L.b_addr[1][1] + FRAG_ROWS);
-    af[1] = read_frag(cur, L.a_addr[1][0] + FRAG_ROWS, L.a_addr[1][1] + FRAG_ROWS);
-    mfma_row<2>(acc, bf0, af[2], sb_k, sa_k);
-    af[2] = read_frag(cur, L.a_addr[1][0] + 2 * FRAG_ROWS, L.a_addr[1][1] + 2 * FRAG_ROWS);
-    mfma_row<3>(acc, bf0, af[3], sb_k, sa_k);
-    af[3] = read_frag(cur, L.a_addr[1][0] + 3 * FRAG_ROWS, L.a_addr[1][1] + 3 * FRAG_ROWS);
-    sched_half<0, 0>();
-    // ---- K half 1
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    GFG_SB();
+    LaneOffsets o;
+    o.a0 = o.b0 = dma_lane_offset(L.wave, L.off.K);
+    o.K = L.off.K;
+    GFG_SB();
+    // ---- first half: rows 0..3
+    {
+        u32x4 r[8];
+#pragma unroll
+        for (int m = 0; m < 32; ++m) {
+            const int y = m >> 3, x = m & 7;
+            acc[y][x] = mfma(bc[x], af[y], acc[y][x], sb_k, y, sa0);
+            GFG_SB();
+            if (m < 8) {
+                const int q = m, yy = 4 + (q >> 1);
+                r[q] = lds16(cur, (q & 1) ? frag_off(L.a_hi_e, L.a_hi_o, yy) : frag_off(L.a_lo_e, L.a_lo_o, yy));
+                GFG_SB();
+            }
+            if (m >= 8 && !(m & 1)) {
+                const int q = (m - 8) >> 1;   // 0..11: A chunks 0, 1, 4, 5 (fragment rows 0..3), then B's
+                if (q < 4)
+                    dma_chunk(rf, o, cur, kr, L.wave, (q & 1) + 4 * (q >> 1));
+                else
+                    dma_chunk_b(rf, o, cur_b, kr, L.wave, q - 4);
+                GFG_SB();
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) af[4 + f] = join(r[2 * f], r[2 * f + 1]);
+    }
+    // ---- mid barrier, then the second half: rows 4..7
     GFG_WAITCNT(VMWAIT, 0);
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_row<0>(acc, bf1, af[0], sb_k, sa_k);
-    bf0[0] = read_frag(nxt, L.b_addr[0][0], L.b_addr[0][1]);
-    dma_stage(rf, L.off, cur, kr, L.wave);
-    af[0] = read_frag(nxt, L.a_addr[0][0], L.a_addr[0][1]);
-    mfma_row<1>(acc, bf1, af[1], sb_k, sa_k);
-    bf0[1] = read_frag(nxt, L.b_addr[0][0] + FRAG_ROWS, L.b_addr[0][1] + FRAG_ROWS);
-    af[1] = read_frag(nxt, L.a_addr[0][0] + FRAG_ROWS, L.a_addr[0][1] + FRAG_ROWS);
-    mfma_row<2>(acc, bf1, af[2], sb_k, sa_k);
-    af[2] = read_frag(nxt, L.a_addr[0][0] + 2 * FRAG_ROWS, L.a_addr[0][1] + 2 * FRAG_ROWS);
-    mfma_row<3>(acc, bf1, af[3], sb_k, sa_k);
-    af[3] = read_frag(nxt, L.a_addr[0][0] + 3 * FRAG_ROWS, L.a_addr[0][1] + 3 * FRAG_ROWS);
+    GFG_SB();
+    if constexpr (FIRST) {
+        const u32x4 lw[2] = {lay[0], lay[1]};
+        // parked in LDS until the epilogue: a register held through the K
+        // loop would be spilled
+        okm[L.wave * 64 + lane_now()] = uint8_t(row_mask<MASKED>(L, lw, lim, g));
+        GFG_SB();
+    }
+    {
+        u32x4 r[24];
+#pragma unroll
+        for (int m = 0; m < 32; ++m) {
+            const int y = 4 + (m >> 3), x = m & 7;
+            acc[y][x] = mfma(bc[x], af[y], acc[y][x], sb_k, y, sa1);
+            GFG_SB();
+            if ((m & 7) == 1) dma_chunk(rf, o, cur, kr, L.wave, 2 + ((m >> 3) & 1) + 4 * (m >> 4));   // 2, 3, 6, 7
+            if (m < 24) {
+                if (m < 16) {   // B fragment m >> 1, chunk m & 1
+                    const int xx = m >> 1;
+                    r[m] = lds16(nxt, (m & 1) ? frag_off(L.b_hi_e, L.b_hi_o, xx) : frag_off(L.b_lo_e, L.b_lo_o, xx));
+                } else {        // A fragment (m - 16) >> 1
+                    const int yy = (m - 16) >> 1;
+                    r[m] = lds16(nxt, (m & 1) ? frag_off(L.a_hi_e, L.a_hi_o, yy) : frag_off(L.a_lo_e, L.a_lo_o, yy));
+                }
+            }
+            GFG_SB();
+        }
+#pragma unroll
+        for (int f = 0; f < 8; ++f) bn[f] = join(r[2 * f], r[2 * f + 1]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) af[f] = join(r[16 + 2 * f], r[17 + 2 * f]);
+    }
     // stage kr's scales replace stage k's, whose last MFMAs are issued above
     load_scales(rf, kr, rows, L.sa_off, sa[PAR], sbw[PAR], sbs[PAR]);
-    sched_half<0, DMA_OPS / 4>();
-    __builtin_amdgcn_sched_group_barrier(0x020, DMA_OPS - 4 * (DMA_OPS / 4) + SL, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    GFG_SB();
 }
 
 template <bool MASKED, typename OutT>
@@ -280,22 +393,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
     __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGE];
     __shared__ uint32_t work[CAND_MAX];      // work tiles in M order
+    __shared__ uint8_t okm_smem[NTHREADS];   // per lane: the row mask of the tile
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     GFG_LDS uint8_t* const buf0 = (GFG_LDS uint8_t*)smem0;
+    GFG_LDS uint8_t* const okm_lds = (GFG_LDS uint8_t*)okm_smem;
     GFG_LDS uint8_t* const buf1 = (GFG_LDS uint8_t*)smem1;
 
     // ---- 1. work tiles (the list build uses stage buffer 0 before the first DMA)
     GFG_LDS int16_t* const expo = reinterpret_cast<GFG_LDS int16_t*>(buf0);   // [CAND_MAX]
     GFG_LDS int* const tmp = reinterpret_cast<GFG_LDS int*>(buf0 + 2 * CAND_MAX);
-    const int c0 = tid * 8;       // this thread's 8 consecutive candidates
+    const int c0 = tid * CPT;     // this thread's CPT consecutive candidates
     unsigned wmask = 0;           // bit j: candidate c0 + j starts a work tile
     unsigned hmask = 0;           // contiguous: ... that has only 128 rows (its run ends with it)
     if (MASKED) {
         // candidate g * mt_per_group + j: rows [256 j, 256 j + 256) of group g
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < CPT; ++j) {
             const int c = c0 + j;
             if (c < p.n_cand) {
                 const int g = c / p.mt_per_group;
@@ -309,7 +424,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
         // that of its first row.  A run is a maximal stretch of candidates of
         // one expert; work tiles start at even offsets inside a run.
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < CPT; ++j) {
             const int c = c0 + j;
             if (c < p.n_cand) {
                 const int e = p.meta[int64_t(c) * 128];
@@ -320,7 +435,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
         int last_start = -1;
         int e_prev = (c0 > 0 && c0 - 1 < p.n_cand) ? int(expo[c0 - 1]) : -1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < CPT; ++j) {
             const int c = c0 + j;
             if (c < p.n_cand) {
                 const int e = expo[c];
@@ -332,7 +447,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
         int run_start = block_exclusive_scan<true>(last_start, tmp, lane, wave, &unused);
         e_prev = (c0 > 0 && c0 - 1 < p.n_cand) ? int(expo[c0 - 1]) : -1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < CPT; ++j) {
             const int c = c0 + j;
             if (c < p.n_cand) {
                 const int e = expo[c];
@@ -348,7 +463,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
     int n_work;
     int off = block_exclusive_scan<false>(__popc(wmask), tmp, lane, wave, &n_work);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < CPT; ++j)
         if ((wmask >> j) & 1u) {
             const int c = c0 + j;
             uint32_t e;
@@ -369,42 +484,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
     const unsigned T = unsigned(n_work) * unsigned(NT);
     TileOrder order;
     order.init(T, p.num_xcd);
+    // uniform: kept in scalar registers (in vector registers they are spilled
+    // and reloaded at every tile)
+    order.x_start = __builtin_amdgcn_readfirstlane(order.x_start);
+    order.x_count = __builtin_amdgcn_readfirstlane(order.x_count);
+    order.slot = __builtin_amdgcn_readfirstlane(order.slot);
+    order.slots = __builtin_amdgcn_readfirstlane(order.slots);
     const unsigned gm = p.group_m > 0 ? unsigned(p.group_m) : 4u;
     unsigned i = order.slot;
     if (i >= order.x_count) return;
 
     Lane L;
     L.wave = wave;
-    L.wm = wave >> 2;
-    L.wn = wave & 3;
-    const int pl = lane & 31, h = lane >> 5, key = (pl >> 1) & 7;
-    L.sa_off = L.wm * 128 + 4 * pl;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = ((4 * kh + 2 * h + j) ^ key) << 4;
-            L.a_addr[kh][j] = (L.wm * 128 + pl) * BK + c;
-            L.b_addr[kh][j] = A_BYTES + (L.wn * 64 + pl) * BK + c;
-        }
-    // DMA sources.  LDS rows are 128 bytes; the physical chunk (lane & 7) of
-    // row R holds logical chunk (lane & 7) ^ ((R >> 1) & 7).
-    // A: row R holds tile row 128 (R >> 7) + 4 (R & 31) + ((R >> 5) & 3), so
-    // that fragment y's lane row p is tile row 4p + y.
-    // B: row R = 64 wn' + 32 x + i holds tile column 64 wn' + 32 x + 16 ((i >> 2) & 1) + 4 (i >> 3) + (i & 3),
-    // so that the MFMA hands lane (p, h) columns 32 x + 16 h .. +15 of one output row.
-#pragma unroll
-    for (int j = 0; j < A_DMA; ++j) {
-        const int R = 8 * (j * WAVES + wave) + (lane >> 3);
-        const int tr = (R >> 7) * 128 + 4 * (R & 31) + ((R >> 5) & 3);
-        L.off.a[j] = uint32_t(tr) * uint32_t(p.K) + uint32_t(((lane & 7) ^ ((R >> 1) & 7)) << 4);
+    L.wm = wave >> 1;
+    L.wn = wave & 1;
+    const int l16 = lane & 15, lq = lane >> 4, odd = l16 & 1;
+    L.sa_off = L.wm * 128 + 4 * l16;
+    {
+        const int p0 = L.wm * 128 + 4 * l16, pb = L.wn * 128 + 4 * l16;
+        L.a_lo_e = swz_a(p0, lq) + odd * BK;
+        L.a_lo_o = swz_a(p0, lq) - odd * BK;
+        L.a_hi_e = swz_a(p0, lq + 4) + odd * BK;
+        L.a_hi_o = swz_a(p0, lq + 4) - odd * BK;
+        L.b_lo_e = A_BYTES + swz_a(pb, lq) + odd * BK;
+        L.b_lo_o = A_BYTES + swz_a(pb, lq) - odd * BK;
+        L.b_hi_e = A_BYTES + swz_a(pb, lq + 4) + odd * BK;
+        L.b_hi_o = A_BYTES + swz_a(pb, lq + 4) - odd * BK;
     }
-#pragma unroll
-    for (int j = 0; j < B_DMA; ++j) {
-        const int R = 8 * (j * WAVES + wave) + (lane >> 3);
-        const int ii = R & 31;
-        const int col = (R >> 5) * 32 + 16 * ((ii >> 2) & 1) + 4 * (ii >> 3) + (ii & 3);
-        L.off.b[j] = uint32_t(col) * uint32_t(p.K) + uint32_t(((lane & 7) ^ ((R >> 1) & 7)) << 4);
+    // DMA sources: chunk 0 of this wave covers LDS rows R = 8 wave + (lane >> 3);
+    // lane i writes physical chunk i % 8, the logical chunk (i % 8) ^ ((R >> 2) & 7)
+    // of tile row a_row(R).
+    {
+        const int R = 8 * wave + (lane >> 3);
+        const uint32_t ch = uint32_t(((lane & 7) ^ ((R >> 2) & 7)) << 4);
+        L.off.a0 = uint32_t(a_row(R)) * uint32_t(p.K) + ch;
+        L.off.b0 = uint32_t(a_row(R)) * uint32_t(p.K) + ch;
+        L.off.K = uint32_t(p.K);
     }
 
     const int KB = p.K / BK;   // even and >= 2 (checked on the host)
@@ -414,23 +529,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
     TileInfo cur = tile_info<MASKED>(p, work[mr], nt);
     Refill rf = make_refill<MASKED>(p, cur, L.wn);
 
-    v16f acc[4][2];
-    v8i af[4], bf0[2], bf1[2];
-    int sa[2], sbw[2], sbs[2];
-    u32x4 lay = u32x4{0u, 0u, 0u, 0u};
+    v4f acc[8][8];
+    v8i af[8], bf0[8], bf1[8];
+    int sa[2][2], sbw[2], sbs[2];
+    u32x4 lay[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
     typedef OutT out8 __attribute__((ext_vector_type(8)));
     typedef float f8v __attribute__((ext_vector_type(8)));
 
-    // ---- prologue: stages 0 and 1 of the first tile, then the tile-boundary
-    // slot of the vector-memory stream: 16 stores that the hardware drops (a
-    // window of zero bytes) and the layout rows of the tile
     // ---- the first tile's start: stages 0 and 1, then the tile-boundary slot
-    // of the vector-memory stream as every later tile has it: 16 stores that
-    // the hardware drops (a window of zero bytes; distinct offsets, so that
-    // none is merged away) and the tile's layout rows; then stage 0's
-    // fragments of K half 0
-    // (The wait below counts everything issued after stage 0's loads; the
-    // scheduler barriers keep that issue order.)
+    // of the vector-memory stream as every later tile has it: the tile's
+    // layout rows and 32 stores that the hardware drops (a window of zero
+    // bytes; distinct offsets, so that none is merged away); then stage 0's
+    // A fragments 0..3 and B fragments.  (The wait below counts everything
+    // issued after stage 0's loads; the scheduler barriers keep that issue
+    // order.)
     __builtin_amdgcn_sched_barrier(0);
     dma_stage(rf, L.off, buf0, 0, wave);
     __builtin_amdgcn_sched_barrier(0);
@@ -440,28 +552,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
     __builtin_amdgcn_sched_barrier(0);
     {
         const __amdgpu_buffer_rsrc_t none = make_rsrc(p.d, 0);
-#pragma unroll
-        for (int s = 0; s < 16; ++s)
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, none, 0x80000000u + 16u * uint32_t(s), 0, 0);
         if (!MASKED) {
             const __amdgpu_buffer_rsrc_t mr_ = make_rsrc(p.meta + cur.row0, uint32_t(cur.lim) * 4u);
-            lay = __builtin_amdgcn_raw_buffer_load_b128(mr_, uint32_t(L.sa_off) * 4u, 0, 0);
+            lay[0] = __builtin_amdgcn_raw_buffer_load_b128(mr_, uint32_t(L.sa_off) * 4u, 0, 0);
+            lay[1] = __builtin_amdgcn_raw_buffer_load_b128(mr_, uint32_t(L.sa_off + 64) * 4u, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 32; ++s)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, none, 0x80000000u + 16u * uint32_t(s), 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     GFG_WAITCNT(2 * SL + DMA_OPS + Epi<MASKED>::OPS, 15);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int y = 0; y < 4; ++y)
-        af[y] = read_frag(buf0, L.a_addr[0][0] + y * FRAG_ROWS, L.a_addr[0][1] + y * FRAG_ROWS);
+        af[y] = join(lds16(buf0, frag_off(L.a_lo_e, L.a_lo_o, y)), lds16(buf0, frag_off(L.a_hi_e, L.a_hi_o, y)));
 #pragma unroll
-    for (int x = 0; x < 2; ++x) bf0[x] = read_frag(buf0, L.b_addr[0][0] + x * FRAG_ROWS, L.b_addr[0][1] + x * FRAG_ROWS);
+    for (int x = 0; x < 8; ++x)
+        bf0[x] = join(lds16(buf0, frag_off(L.b_lo_e, L.b_lo_o, x)), lds16(buf0, frag_off(L.b_hi_e, L.b_hi_o, x)));
 
     while (true) {
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
+        for (int y = 0; y < 8; ++y)
 #pragma unroll
-            for (int x = 0; x < 2; ++x) acc[y][x] = v16f{};
+            for (int x = 0; x < 8; ++x) acc[y][x] = v4f{};
+        i = __builtin_amdgcn_readfirstlane(i);
         const unsigned i_next = i + order.slots;
         const bool have_next = i_next < order.x_count;
         // the next tile, decoded here (its divisions stay out of the K loop)
@@ -476,92 +592,104 @@ __global__ __launch_bounds__(NTHREADS, 1) void grouped_fp8_gemm256_kernel(Params
         // that stage expects), or, on the last tile, a dummy copy of the last stage.
         // The loop runs at least once (KB >= 2), which the compiler is told, so
         // its own waits at the tile boundary count the boundary's operations.
+        // The tile's first pair of steps is peeled: its second-half wait also
+        // counts the tile-boundary operations.  (A run-time choice of the wait
+        // inside the step would put a branch between the halves, and the
+        // compiler then moves the first half's MFMAs past the barrier.)
         int kb = 0;
-        do {
-            if (kb + 2 == KB && have_next) rf = make_refill<MASKED>(p, next, L.wn);
-            const int kr0 = kb + 2 < KB ? kb + 2 : (have_next ? kb + 2 - KB : KB - 1);
-            const int kr1 = kb + 3 < KB ? kb + 3 : (have_next ? kb + 3 - KB : KB - 1);
-            if (kb == 0)
-                k_step<0, SL + Epi<MASKED>::OPS>(L, int(p.rows), buf0, buf1, kr0, rf, acc, af, bf0, bf1, sa, sbw, sbs);
+        auto refills = [&](int k, int& r0, int& r1) {
+            if (k + 2 == KB && have_next) rf = make_refill<MASKED>(p, next, L.wn);
+            r0 = k + 2 < KB ? k + 2 : (have_next ? k + 2 - KB : KB - 1);
+            r1 = k + 3 < KB ? k + 3 : (have_next ? k + 3 - KB : KB - 1);
+        };
+        {
+            int kr0, kr1;
+            refills(0, kr0, kr1);
+            if constexpr (MASKED)
+                k_step<0, SL + FIRST_HALF_DMA + Epi<MASKED>::OPS>(L, int(p.rows), buf0, buf0 + A_BYTES, buf1, kr0, rf, acc, af, bf0, bf1, sa, sbw, sbs);
             else
-                k_step<0, SL>(L, int(p.rows), buf0, buf1, kr0, rf, acc, af, bf0, bf1, sa, sbw, sbs);
-            k_step<1, SL>(L, int(p.rows), buf1, buf0, kr1, rf, acc, af, bf0, bf1, sa, sbw, sbs);
-            kb += 2;
-        } while (kb < KB);
+                k_step<0, SL + FIRST_HALF_DMA + Epi<MASKED>::OPS, MASKED, true>(L, int(p.rows), buf0, buf0 + A_BYTES, buf1, kr0, rf, acc, af, bf0, bf1,
+                                                                sa, sbw, sbs, okm_lds, lay, cur.lim, cur.g);
+            k_step<1, SL + FIRST_HALF_DMA>(L, int(p.rows), buf1, buf1 + A_BYTES, buf0, kr1, rf, acc, af, bf1, bf0, sa, sbw, sbs);
+            kb = 2;
+        }
 
-        // ---- epilogue.  Lane (p, h) holds, for each y, output row 128 wm + 4p + y,
-        // columns 64 wn + 32 x + 16 h .. +15 (acc[y][x]): the 16-byte chunks
-        // 4x + 2h + jj (jj: which 8 columns) of that row's 128-byte line.  A 4 x 4
-        // transpose inside each lane quad (slot s = 2x + jj against lane bits 0
-        // and 1, by DPP) hands lane 4q + j, slot s, chunk 4 (j >> 1) + 2h + (j & 1)
-        // of row 16q + 4s + y, so every store instruction writes eight whole
-        // lines; those go out non-temporal.
+        while (kb < KB) {
+            int kr0, kr1;
+            refills(kb, kr0, kr1);
+            k_step<0, SL + FIRST_HALF_DMA>(L, int(p.rows), buf0, buf0 + A_BYTES, buf1, kr0, rf, acc, af, bf0, bf1, sa, sbw, sbs);
+            k_step<1, SL + FIRST_HALF_DMA>(L, int(p.rows), buf1, buf1 + A_BYTES, buf0, kr1, rf, acc, af, bf1, bf0, sa, sbw, sbs);
+            kb += 2;
+        }
+
+        // ---- epilogue.  Lane (l16, lq) holds, for each y, output row
+        // 128 wm + 64 (y >> 2) + 4 l16 + (y & 3), and for each column half hx
+        // the 16 columns 128 wn + 64 hx + 16 lq .. +15 (acc[y][4 hx + x][i] is
+        // column 16 lq + 4 i + x): the 16-byte chunks 2 lq and 2 lq + 1 of that
+        // row's 128-byte line.  Swapping lane bit 0 with the chunk (DPP
+        // quad_perm 1,0,3,2) hands slot h of lane (l16, lq) chunk 2 lq + (l16 & 1)
+        // of row 4 ((l16 & ~1) | h) + y, so every store instruction writes eight
+        // whole lines; those go out non-temporal.
+        // The next tile's layout words are loaded first: they complete before
+        // the stores (completion follows issue order), so the next tile's
+        // first step can use them without waiting for the stores.  After the
+        // last tile the window is empty: the loads return zeros and touch no
+        // memory, and no branch splits the stores.
+        if (!MASKED) {
+            const __amdgpu_buffer_rsrc_t mr_ =
+                make_rsrc(p.meta + next.row0, have_next ? uint32_t(next.lim) * 4u : 0u);
+            lay[0] = __builtin_amdgcn_raw_buffer_load_b128(mr_, uint32_t(L.sa_off) * 4u, 0, 0);
+            lay[1] = __builtin_amdgcn_raw_buffer_load_b128(mr_, uint32_t(L.sa_off + 64) * 4u, 0, 0);
+        }
+        GFG_SB();
         const int64_t out_row0 = (MASKED ? int64_t(cur.g) * p.rows : 0) + cur.row0;
         const __amdgpu_buffer_rsrc_t dr = make_rsrc(reinterpret_cast<uint8_t*>(p.d) + (out_row0 * p.N + cur.n0) * 2,
                                                     uint32_t(BM) * uint32_t(p.N) * 2u);
-        // bit y: the lane's own row 128 wm + 4p + y may be written; then, per
-        // slot s, the bits of quad lane s (whose rows that slot now holds)
-        int okm = 0;
+        const int ln = lane_now();
+        // bit y: the lane's own row for y may be written (the masked layout's
+        // rows end at the tile's limit; the contiguous layout's also belong to
+        // the tile's group)
+        const int okm = MASKED ? row_mask<true>(L, lay, cur.lim, cur.g) : int(okm_lds[L.wave * 64 + ln]);
+        // per slot h, the row bits of the pair lane whose rows the slot now holds
+        const int okh[2] = {__builtin_amdgcn_update_dpp(0, okm, 0xA0, 0xF, 0xF, false),
+                            __builtin_amdgcn_update_dpp(0, okm, 0xF5, 0xF, 0xF, false)};
+        const bool odd = (ln & 1) != 0;
+        const uint32_t rbase = uint32_t(L.wm * 128 + 4 * ((ln & 15) & ~1));
+        const uint32_t colb = uint32_t((L.wn * 128 + 16 * (ln >> 4) + 8 * (ln & 1)) * 2);
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
-            okm |= int(L.sa_off + y < cur.lim && (MASKED || int(lay[y]) == cur.g)) << y;
-        const int okq[4] = {__builtin_amdgcn_update_dpp(0, okm, 0x00, 0xF, 0xF, false),
-                            __builtin_amdgcn_update_dpp(0, okm, 0x55, 0xF, 0xF, false),
-                            __builtin_amdgcn_update_dpp(0, okm, 0xAA, 0xF, 0xF, false),
-                            __builtin_amdgcn_update_dpp(0, okm, 0xFF, 0xF, 0xF, false)};
-        const bool j0 = (lane & 1) != 0, j1 = (lane & 2) != 0;
-        const uint32_t qrow = uint32_t(L.wm * 128 + 16 * ((lane & 31) >> 2));
-        const uint32_t colb = uint32_t(L.wn * 128 + 16 * (4 * ((lane >> 1) & 1) + 2 * h + (lane & 1)));
+        for (int y = 0; y < 8; ++y)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            uint32_t P[4][4];
+            for (int hx = 0; hx < 2; ++hx) {
+                u32x4 P[2];
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const v16f& a = acc[y][x];
-                    const f8v v = {a[8 * jj + 0], a[8 * jj + 1], a[8 * jj + 2], a[8 * jj + 3],
-                                   a[8 * jj + 4], a[8 * jj + 5], a[8 * jj + 6], a[8 * jj + 7]};
-                    const u32x4 o = __builtin_bit_cast(u32x4, __builtin_convertvector(v, out8));
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) P[2 * x + jj][d] = o[d];
+                for (int hh = 0; hh < 2; ++hh) {
+                    const v4f c0 = acc[y][4 * hx], c1 = acc[y][4 * hx + 1], c2 = acc[y][4 * hx + 2],
+                              c3 = acc[y][4 * hx + 3];
+                    const f8v v = {c0[2 * hh], c1[2 * hh], c2[2 * hh], c3[2 * hh],
+                                   c0[2 * hh + 1], c1[2 * hh + 1], c2[2 * hh + 1], c3[2 * hh + 1]};
+                    P[hh] = __builtin_bit_cast(u32x4, __builtin_convertvector(v, out8));
                 }
-            // swap lane bit 0 with slot bit 0 (quad_perm 1,0,3,2), then lane bit 1
-            // with slot bit 1 (quad_perm 2,3,0,1)
-#pragma unroll
-            for (int s1 = 0; s1 < 2; ++s1)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const uint32_t a = P[2 * s1][d], b = P[2 * s1 + 1][d];
+                    const uint32_t a = P[0][d], b = P[1][d];
                     const uint32_t ax = uint32_t(__builtin_amdgcn_update_dpp(0, int(a), 0xB1, 0xF, 0xF, false));
                     const uint32_t bx = uint32_t(__builtin_amdgcn_update_dpp(0, int(b), 0xB1, 0xF, 0xF, false));
-                    P[2 * s1][d] = j0 ? bx : a;
-                    P[2 * s1 + 1][d] = j0 ? b : ax;
+                    P[0][d] = odd ? bx : a;
+                    P[1][d] = odd ? b : ax;
                 }
 #pragma unroll
-            for (int s0 = 0; s0 < 2; ++s0)
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t a = P[s0][d], b = P[2 + s0][d];
-                    const uint32_t ax = uint32_t(__builtin_amdgcn_update_dpp(0, int(a), 0x4E, 0xF, 0xF, false));
-                    const uint32_t bx = uint32_t(__builtin_amdgcn_update_dpp(0, int(b), 0x4E, 0xF, 0xF, false));
-                    P[s0][d] = j1 ? bx : a;
-                    P[2 + s0][d] = j1 ? b : ax;
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t row = rbase + uint32_t(4 * hh + 64 * (y >> 2) + (y & 3));
+                    // a row that may not be written gets bit 31, past the
+                    // window's end (the offset itself stays below 2^31)
+                    const uint32_t voff = (row * uint32_t(p.N) * 2u + colb + uint32_t(128 * hx)) |
+                                          ((~uint32_t(okh[hh]) >> y) << 31);
+                    __builtin_amdgcn_raw_buffer_store_b128(P[hh], dr, voff, 0, 2 /* nt */);
                 }
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint32_t row = qrow + uint32_t(4 * s + y);
-                const uint32_t voff = ((okq[s] >> y) & 1) ? row * uint32_t(p.N) * 2u + colb : 0x80000000u;
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4{P[s][0], P[s][1], P[s][2], P[s][3]}, dr, voff, 0,
-                                                       2 /* nt */);
+                GFG_SB();
             }
-        }
         if (!have_next) break;
         cur = next;
-        if (!MASKED) {
-            const __amdgpu_buffer_rsrc_t mr_ = make_rsrc(p.meta + cur.row0, uint32_t(cur.lim) * 4u);
-            lay = __builtin_amdgcn_raw_buffer_load_b128(mr_, uint32_t(L.sa_off) * 4u, 0, 0);
-        }
         i = i_next;
     }
     GFG_WAITCNT(0, 0);   // the dummy refills of the last steps land before the workgroup ends
