@@ -853,17 +853,22 @@ int dispatch(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
         }
         // Automatic choice (from timings of both shapes): the 256 x 256 tile
         // pays a larger fixed cost per launch (its first stages and last
-        // output stores are not overlapped with MFMAs) and a quarter of its
-        // tile is idle on the half tiles at run ends, so it wins when every CU
-        // walks at least four of its tiles, or one of them with a long K loop
-        // (64 steps or more).  Masked launches count from the host-side upper
-        // bound (masked_m lives in device memory), so only the first rule
-        // applies to them.
+        // output stores are not overlapped with MFMAs) and its bottom half is
+        // idle on the 128-row tiles at run ends, so it wins when every CU
+        // walks at least two of its tiles (measured from 2 to 14 per CU: 6 to
+        // 14% faster; at one per CU or fewer the 128 x 256 kernel is faster),
+        // or one of them with a long K loop (64 steps or more).  For the
+        // contiguous layout the experts' runs must also average at least two
+        // 128-row tiles, or most 256-row tiles would be half tiles (the host
+        // sees only the total, grouped_layout lives in device memory).
+        // Masked launches count from the host-side upper bound (masked_m
+        // lives in device memory too), so only the first rule applies to them.
         const uint64_t tiles = uint64_t(MASKED ? nc : (n_cand + 1) / 2) * unsigned(p.N / 256);
         int cus = 0;
         if (int rc = device_cus(&cus)) return rc;
-        const bool many = tiles >= 4 * uint64_t(cus);
-        const bool long_k = !MASKED && tiles >= uint64_t(cus) && p.K / BK >= 64;
+        const bool runs = MASKED || n_cand >= 2 * unsigned(p.G);
+        const bool many = runs && tiles >= 2 * uint64_t(cus);
+        const bool long_k = !MASKED && runs && tiles >= uint64_t(cus) && p.K / BK >= 64;
         if (choice == GFG_TILE_256x256 || many || long_k) return launch_gemm256(q, MASKED, nc, out_dtype, s);
     }
     return saw ? dispatch_w<MASKED, true>(p, n_cand, out_dtype, s) : dispatch_w<MASKED, false>(p, n_cand, out_dtype, s);

@@ -116,9 +116,9 @@ def _no_stray_sentinel(b_rows, ref, out_dtype, what):
 
 
 # The FP8 workloads again with the tile shape the automatic choice does not
-# take, forced: the 256 x 256 kernel on the one-round, ragged and masked
-# shapes, the 128 x 256 kernel on the many-tile and long-K ones.
-_OTHER = {"contig_g4_m1024_n2048_k7168": gfg.TILE_256x256, "contig_g8_mrand_n7168_k2304": gfg.TILE_256x256,
+# take, forced: the 256 x 256 kernel on the one-round and masked shapes, the
+# 128 x 256 kernel on the many-tile (including the ragged one) and long-K ones.
+_OTHER = {"contig_g4_m1024_n2048_k7168": gfg.TILE_256x256, "contig_g8_mrand_n7168_k2304": gfg.TILE_128x256,
           "masked_g8_m1024_n2048_k7168": gfg.TILE_256x256,
           "contig_g8_m4096_n7168_k2304_logmag": gfg.TILE_128x256, "dense_g1_m4096_n4096_k16384": gfg.TILE_128x256}
 _OTHER_CASES = [(n, c) for n in _OTHER for c in range(_chunks(wl.workload(n)))]
