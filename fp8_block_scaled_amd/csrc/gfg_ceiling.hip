@@ -14,12 +14,12 @@
 namespace gfg {
 namespace {
 
-constexpr int CEIL_THREADS = 512;   // 8 wave64s per CU, as in the GEMM kernels
+constexpr int CEIL_THREADS = 512;   // 8 wave64s per CU, as in the 128-row GEMM kernel
 constexpr int CEIL_FRAGS = 12;      // fragments per wave: 8 A (two K halves), 4 B
 
 // Each wave keeps twelve 32-byte-per-lane operand fragments loaded from
 // `ops` (real E4M3 data, so the matrix pipes switch as in the GEMM) and issues
-// the 256 x 256 tile's per-wave MFMA pattern of one 128-K step, 16
+// a 128 x 64 wave tile's MFMA pattern of one 128-K step, 16
 // v_mfma_scale_f32_32x32x64_f8f6f4 on eight accumulators, `iters` times.
 // Scales are 127 (2^0).  Each thread writes one float (the sum of its
 // accumulators) to `sink`, so that nothing is optimized away.
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(CEIL_THREADS, 1) void mfma_ceiling_kernel(const uin
 }
 
 // The same operands, FLOPs and waves with v_mfma_scale_f32_16x16x128_f8f6f4
-// (the 128-row GEMM kernel's instruction): per iteration each wave issues 32 of
+// (the instruction of both GEMM kernels): per iteration each wave issues 32 of
 // them, A fragments 0..3 against B fragments 4..11, on 32 four-register
 // accumulators.
 __global__ __launch_bounds__(CEIL_THREADS, 1) void mfma16_ceiling_kernel(const uint8_t* __restrict__ ops, int iters,

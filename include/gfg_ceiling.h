@@ -37,7 +37,7 @@ GFG_API int64_t gfg_ceiling_mfma_operand_bytes(void);
 
 /*
  * The scaled-MFMA ceiling: one workgroup of 8 wave64s per CU, each wave
- * issuing the 256 x 256 GEMM tile's per-wave pattern of one 128-K step
+ * issuing the MFMA pattern of a 128 x 64 wave tile's 128-K step
  * (16 v_mfma_scale_f32_32x32x64_f8f6f4 on 8 accumulators) `iters` times, on
  * register operands loaded once from `operands` (E4M3 bytes; pass real
  * quantized data, as the matrix pipes' power, and so the clock, depends on
@@ -54,8 +54,8 @@ GFG_API int gfg_ceiling_mfma(const uint8_t* operands, int64_t operand_bytes, int
                              int64_t sink_floats, double* flops, void* stream);
 
 /*
- * The same measurement with v_mfma_scale_f32_16x16x128_f8f6f4, the 128-row
- * kernel's instruction: the same operands (gfg_ceiling_mfma_operand_bytes()),
+ * The same measurement with v_mfma_scale_f32_16x16x128_f8f6f4, the
+ * instruction of both GEMM kernels: the same operands (gfg_ceiling_mfma_operand_bytes()),
  * waves and FLOPs per iteration (each wave issues 32 of them on 32
  * four-register accumulators), the same sink and argument rules.  On the same
  * bytes this shape runs faster than 32x32x64 (measured on MI355X: about 4720
