@@ -319,14 +319,15 @@ GFG_API int fp8_quantize_act_1x128_device(const void* x, int32_t in_dtype, int32
  *
  * grouped_fp8_set_tile_shape: the output tile of the plain FP8 GEMM calls
  * (grouped_fp8_gemm_contiguous / _masked).  GFG_TILE_AUTO picks 256 x 256
- * (where its requirements hold) when the launch has at least four such tiles
+ * (where its requirements hold) when the launch has at least two such tiles
  * per CU, or, for the contiguous layout, at least one per CU and K >= 8192;
- * else 128 x 256.  (The masked layout counts from M_max: masked_m is device
- * memory.)  GFG_TILE_256x256 needs N a multiple of 256 and
+ * for the contiguous layout the rows must also average at least two 128-row
+ * tiles per expert; else 128 x 256.  (The masked layout counts from M_max:
+ * masked_m is device memory.)  GFG_TILE_256x256 needs N a multiple of 256 and
  * at most 2^22, K/128 even, scale rows a multiple of 4 and scale_a 4-byte
  * aligned; a call that misses them then returns GFG_EUNSUPPORTED.  Other
- * values: GFG_EINVAL.  Results agree to the parity tolerance, not bit for
- * bit: the two tiles sum each 128-K block's products in different groupings.
+ * values: GFG_EINVAL.  Results of the two tiles agree to the parity
+ * tolerance; they are not promised to agree bit for bit.
  *
  * grouped_fp8_set_grid_limit: at most max_workgroups workgroups per GEMM
  * launch (0, the default: one per CU, fewer when there are fewer tiles).  The
