@@ -851,25 +851,31 @@ int dispatch(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
             q.n_cand = q.mt_per_group * p.G;
             nc = unsigned(q.n_cand);
         }
-        // Automatic choice (from timings of both shapes): the 256 x 256 tile
-        // pays a larger fixed cost per launch (its first stages and last
-        // output stores are not overlapped with MFMAs) and its bottom half is
-        // idle on the 128-row tiles at run ends, so it wins when every CU
-        // walks at least two of its tiles (measured from 2 to 14 per CU: 6 to
-        // 14% faster; at one per CU or fewer the 128 x 256 kernel is faster),
-        // or one of them with a long K loop (64 steps or more).  For the
-        // contiguous layout the experts' runs must also average at least two
-        // 128-row tiles, or most 256-row tiles would be half tiles (the host
-        // sees only the total, grouped_layout lives in device memory).
-        // Masked launches count from the host-side upper bound (masked_m
-        // lives in device memory too), so only the first rule applies to them.
-        const uint64_t tiles = uint64_t(MASKED ? nc : (n_cand + 1) / 2) * unsigned(p.N / 256);
+        // Automatic choice (from timings of both shapes on 26 shapes): one
+        // 256 x 256 tile takes about 1.6 times as long as one 128 x 256 tile
+        // (1.5 to 1.9 measured), so the 256 x 256 kernel wins when its rounds
+        // of tiles over the CUs, times 1.6, are at most the 128 x 256 one's
+        // (two rounds against three loses by 5%; one against two, three
+        // against five and four against seven win by 4 to 14%).  A single
+        // round of it also needs a K loop of 32 steps or more, which hides
+        // its fixed cost per tile (the first stages and the epilogue); the
+        // masked layout, counted from the host-side upper bound M_max
+        // (masked_m lives in device memory), needs two of its tiles per CU
+        // by that count instead.  For the contiguous layout the experts'
+        // runs must average at least two 128-row tiles, or most 256-row
+        // tiles would be half tiles (the host sees only the total rows;
+        // grouped_layout lives in device memory too).
+        const uint64_t nt = unsigned(p.N / 256);
+        const uint64_t t256 = uint64_t(MASKED ? nc : (n_cand + 1) / 2) * nt;
+        const uint64_t t128 = uint64_t(n_cand) * nt;
         int cus = 0;
         if (int rc = device_cus(&cus)) return rc;
+        const uint64_t r256 = (t256 + cus - 1) / cus, r128 = (t128 + cus - 1) / cus;
         const bool runs = MASKED || n_cand >= 2 * unsigned(p.G);
-        const bool many = runs && tiles >= 2 * uint64_t(cus);
-        const bool long_k = !MASKED && runs && tiles >= uint64_t(cus) && p.K / BK >= 64;
-        if (choice == GFG_TILE_256x256 || many || long_k) return launch_gemm256(q, MASKED, nc, out_dtype, s);
+        const bool rounds = 8 * r256 <= 5 * r128;   // r256 * 1.6 <= r128
+        const bool enough = MASKED ? t256 >= 2 * uint64_t(cus) : (r256 >= 2 || p.K / BK >= 32);
+        if (choice == GFG_TILE_256x256 || (runs && rounds && enough))
+            return launch_gemm256(q, MASKED, nc, out_dtype, s);
     }
     return saw ? dispatch_w<MASKED, true>(p, n_cand, out_dtype, s) : dispatch_w<MASKED, false>(p, n_cand, out_dtype, s);
 }

@@ -319,11 +319,12 @@ GFG_API int fp8_quantize_act_1x128_device(const void* x, int32_t in_dtype, int32
  *
  * grouped_fp8_set_tile_shape: the output tile of the plain FP8 GEMM calls
  * (grouped_fp8_gemm_contiguous / _masked).  GFG_TILE_AUTO picks 256 x 256
- * (where its requirements hold) when the launch has at least two such tiles
- * per CU, or, for the contiguous layout, at least one per CU and K >= 8192;
- * for the contiguous layout the rows must also average at least two 128-row
- * tiles per expert; else 128 x 256.  (The masked layout counts from M_max:
- * masked_m is device memory.)  GFG_TILE_256x256 needs N a multiple of 256 and
+ * (where its requirements hold) when R256 * 1.6 <= R128, R being the rounds
+ * of each shape's tiles over the CUs (ceil(tiles / CUs)), and either
+ * R256 >= 2 or K >= 4096 (contiguous layout) or at least two 256 x 256 tiles
+ * per CU (masked layout, counted from M_max: masked_m is device memory); for
+ * the contiguous layout the rows must also average at least two 128-row tiles
+ * per expert; else 128 x 256.  GFG_TILE_256x256 needs N a multiple of 256 and
  * at most 2^22, K/128 even, scale rows a multiple of 4 and scale_a 4-byte
  * aligned; a call that misses them then returns GFG_EUNSUPPORTED.  Other
  * values: GFG_EINVAL.  Results of the two tiles agree to the parity
