@@ -18,6 +18,7 @@ weight draws, the rows of every expert that uses one draw.  Per chunk:
 
 The five FP8 GEMM workloads run a second time with the other output tile
 (the one the automatic choice does not pick) forced, to the same checks.
+Four more shapes near the automatic choice's threshold run under it.
 """
 import numpy as np
 import pytest
@@ -124,6 +125,14 @@ _OTHER = {"contig_g4_m1024_n2048_k7168": gfg.TILE_256x256, "contig_g8_mrand_n716
 _OTHER_CASES = [(n, c) for n in _OTHER for c in range(_chunks(wl.workload(n)))]
 
 
+# Shapes near the automatic tile choice's threshold (rounds of tiles over the
+# CUs: 1 against 2 with a long K loop, 2 against 3, 3 against 5, and a masked
+# launch of 3 against 6), every output under the automatic choice.
+_THRESHOLD = ["contig_g8_m1024_n2048_k7168", "contig_g8_m1280_n2048_k7168", "contig_g8_m1280_n4096_k2304",
+              "masked_g8_m1536_n4096_k2304"]
+_THRESHOLD_CASES = [(n, c) for n in _THRESHOLD for c in range(_chunks(wl.workload(n)))]
+
+
 @pytest.mark.parametrize("name,chunk", _CASES, ids=[f"{n}-{c}" for n, c in _CASES])
 def test_full_size_every_output(name, chunk):
     _check_chunk(name, chunk, gfg.TILE_AUTO)
@@ -132,6 +141,11 @@ def test_full_size_every_output(name, chunk):
 @pytest.mark.parametrize("name,chunk", _OTHER_CASES, ids=[f"{n}-{c}" for n, c in _OTHER_CASES])
 def test_full_size_other_tile_shape(name, chunk):
     _check_chunk(name, chunk, _OTHER[name])
+
+
+@pytest.mark.parametrize("name,chunk", _THRESHOLD_CASES, ids=[f"{n}-{c}" for n, c in _THRESHOLD_CASES])
+def test_full_size_tile_choice_threshold(name, chunk):
+    _check_chunk(name, chunk, gfg.TILE_AUTO)
 
 
 def _check_chunk(name, chunk, tile):
