@@ -855,8 +855,9 @@ int dispatch(const Params& p, unsigned n_cand, int out_dtype, hipStream_t s) {
         // 256 x 256 tile takes about 1.6 times as long as one 128 x 256 tile
         // (1.5 to 1.9 measured), so the 256 x 256 kernel wins when its rounds
         // of tiles over the CUs, times 1.6, are at most the 128 x 256 one's
-        // (two rounds against three loses by 5%; one against two, three
-        // against five and four against seven win by 4 to 14%).  A single
+        // (two rounds against three is from 1% faster to 10% slower; one
+        // against two, three against five and four against seven win by 4 to
+        // 14%).  A single
         // round of it also needs a K loop of 32 steps or more, which hides
         // its fixed cost per tile (the first stages and the epilogue); the
         // masked layout, counted from the host-side upper bound M_max
