@@ -336,16 +336,24 @@ __device__ __forceinline__ void k_step(const C& c, GFG_LDS uint8_t* __restrict__
                                              16, 0, 0);
     }
     if (READ) {
+        // MX4: the lane's fragment offsets made opaque here, so that the
+        // compiler adds the stage buffer's base per step instead of holding
+        // one copy of every offset per buffer through the tile (the two
+        // extra scale words per stage leave no registers for those copies)
+        C o = c;
+        if constexpr (C::MX4)
+            asm volatile("" : "+v"(o.a_lo_e), "+v"(o.a_lo_o), "+v"(o.a_hi_e), "+v"(o.a_hi_o), "+v"(o.b_lo_e),
+                         "+v"(o.b_lo_o), "+v"(o.b_hi_e), "+v"(o.b_hi_o));
 #pragma unroll
         for (int y = 0; y < C::FM; ++y) {
-            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + ((y & 1) ? c.a_lo_o : c.a_lo_e) + y * BK);
-            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + ((y & 1) ? c.a_hi_o : c.a_hi_e) + y * BK);
+            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + ((y & 1) ? o.a_lo_o : o.a_lo_e) + y * BK);
+            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + ((y & 1) ? o.a_hi_o : o.a_hi_e) + y * BK);
             nxt.a[y] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
         for (int x = 0; x < C::FN; ++x) {
-            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + b_frag(c, x, false));
-            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + b_frag(c, x, true));
+            const u32x4 l = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + b_frag(o, x, false));
+            const u32x4 h = *reinterpret_cast<const GFG_LDS u32x4*>(next + C::A_BYTES + b_frag(o, x, true));
             nxt.b[x] = __builtin_bit_cast(v8i, __builtin_shufflevector(l, h, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     }
